@@ -1,0 +1,144 @@
+// C-ABI entry points for partial attention: host-side validation, then
+// dispatch to the fp32 kernel, the bf16 MFMA kernel (contiguous or paged
+// prefill) or the split-KV decode kernels. Nothing here touches the GPU
+// before every argument has been checked.
+#include "cpa_internal.h"
+
+using namespace cpa;
+
+namespace {
+
+cpa_status check_common(const char* fn, const void* q, const int32_t* q_pos, const int32_t* cu_q, const void* k,
+                        const void* v, int32_t num_seqs, int32_t max_q, int32_t hq, int32_t hkv, int32_t d,
+                        float scale, int mask, const void* o, const float* lse) {
+  if (num_seqs < 0) return fail(CPA_ERR_INVALID_ARG, "%s: num_seqs < 0", fn);
+  if (max_q < 0) return fail(CPA_ERR_INVALID_ARG, "%s: max_q < 0", fn);
+  if (hq < 1 || hkv < 1 || hq % hkv != 0)
+    return fail(CPA_ERR_INVALID_ARG, "%s: need hq, hkv >= 1 and hq %% hkv == 0 (hq=%d, hkv=%d)", fn, hq, hkv);
+  if (d != 64 && d != 128) return fail(CPA_ERR_UNSUPPORTED, "%s: d = %d (supported: 64, 128)", fn, d);
+  if (!(scale > 0.f) || scale != scale || scale > 1e30f) return fail(CPA_ERR_INVALID_ARG, "%s: bad scale", fn);
+  if (mask != CPA_MASK_NONE && mask != CPA_MASK_CAUSAL) return fail(CPA_ERR_INVALID_ARG, "%s: bad mask", fn);
+  if (num_seqs > 0 && max_q > 0) {
+    if (!q || !cu_q || !k || !v || !o || !lse) return fail(CPA_ERR_INVALID_ARG, "%s: NULL tensor pointer", fn);
+    if (mask == CPA_MASK_CAUSAL && !q_pos) return fail(CPA_ERR_INVALID_ARG, "%s: q_pos is NULL", fn);
+  }
+  return CPA_OK;
+}
+
+}  // namespace
+
+extern "C" cpa_status cpa_partial_attn(const void* q, const int32_t* q_pos, const int32_t* cu_q, const void* k,
+                                       const void* v, const int32_t* k_pos, const int32_t* cu_k, int32_t num_seqs,
+                                       int32_t max_q, int32_t hq, int32_t hkv, int32_t d, cpa_dtype in_dtype,
+                                       float scale, cpa_mask mask, void* o, cpa_dtype o_dtype, float* lse,
+                                       void* stream) {
+  const char* fn = "cpa_partial_attn";
+  cpa_status st = check_common(fn, q, q_pos, cu_q, k, v, num_seqs, max_q, hq, hkv, d, scale, mask, o, lse);
+  if (st != CPA_OK) return st;
+  if (in_dtype != CPA_BF16 && in_dtype != CPA_F32) return fail(CPA_ERR_INVALID_ARG, "%s: bad in_dtype", fn);
+  if (o_dtype != CPA_BF16 && o_dtype != CPA_F32) return fail(CPA_ERR_INVALID_ARG, "%s: bad o_dtype", fn);
+  if (in_dtype == CPA_F32 && o_dtype != CPA_F32)
+    return fail(CPA_ERR_UNSUPPORTED, "%s: fp32 inputs need an fp32 output", fn);
+  if (num_seqs > 0 && max_q > 0) {
+    if (!cu_k) return fail(CPA_ERR_INVALID_ARG, "%s: cu_k is NULL", fn);
+    if (mask == CPA_MASK_CAUSAL && !k_pos) return fail(CPA_ERR_INVALID_ARG, "%s: k_pos is NULL", fn);
+  }
+  st = check_device();
+  if (st != CPA_OK) return st;
+  if (num_seqs == 0 || max_q == 0) return CPA_OK;
+  AttnArgs a;
+  a.q = q;
+  a.q_pos = q_pos;
+  a.cu_q = cu_q;
+  a.k = k;
+  a.v = v;
+  a.k_pos = k_pos;
+  a.cu_k = cu_k;
+  a.num_seqs = num_seqs;
+  a.max_q = max_q;
+  a.hq = hq;
+  a.hkv = hkv;
+  a.d = d;
+  a.scale = scale;
+  a.causal = mask == CPA_MASK_CAUSAL;
+  a.o = o;
+  a.o_bf16 = o_dtype == CPA_BF16;
+  a.lse = lse;
+  hipStream_t s = (hipStream_t)stream;
+  if (in_dtype == CPA_F32) return launch_attn_f32(a, s);
+  return launch_attn_mfma(a, /*paged=*/false, s);
+}
+
+extern "C" cpa_status cpa_partial_attn_paged_workspace(int32_t num_seqs, int32_t max_q, int32_t max_blocks,
+                                                       int32_t block_size, int32_t hq, int32_t d, size_t* bytes) {
+  const char* fn = "cpa_partial_attn_paged_workspace";
+  if (!bytes) return fail(CPA_ERR_INVALID_ARG, "%s: bytes is NULL", fn);
+  if (num_seqs < 0 || max_q < 0 || max_blocks < 0 || hq < 1)
+    return fail(CPA_ERR_INVALID_ARG, "%s: negative size or hq < 1", fn);
+  if (block_size != 16) return fail(CPA_ERR_UNSUPPORTED, "%s: block_size %d (supported: 16)", fn, block_size);
+  if (d != 64 && d != 128) return fail(CPA_ERR_UNSUPPORTED, "%s: d = %d (supported: 64, 128)", fn, d);
+  *bytes = (max_q == 1) ? decode_workspace_bytes(num_seqs, max_blocks, block_size, hq, d) : 0;
+  return CPA_OK;
+}
+
+extern "C" cpa_status cpa_partial_attn_paged(const void* q, const int32_t* q_pos, const int32_t* cu_q,
+                                             const void* k_cache, const void* v_cache, const int32_t* block_table,
+                                             int32_t max_blocks, const int32_t* local_kv_lens, int32_t block_size,
+                                             int32_t cp_size, int32_t cp_rank, int32_t interleave, int32_t num_seqs,
+                                             int32_t max_q, int32_t hq, int32_t hkv, int32_t d, cpa_dtype in_dtype,
+                                             float scale, cpa_mask mask, void* o, cpa_dtype o_dtype, float* lse,
+                                             void* workspace, size_t workspace_bytes, void* stream) {
+  const char* fn = "cpa_partial_attn_paged";
+  cpa_status st =
+      check_common(fn, q, q_pos, cu_q, k_cache, v_cache, num_seqs, max_q, hq, hkv, d, scale, mask, o, lse);
+  if (st != CPA_OK) return st;
+  if (in_dtype != CPA_BF16) return fail(CPA_ERR_UNSUPPORTED, "%s: only bf16 caches are supported", fn);
+  if (o_dtype != CPA_BF16 && o_dtype != CPA_F32) return fail(CPA_ERR_INVALID_ARG, "%s: bad o_dtype", fn);
+  if (block_size != 16) return fail(CPA_ERR_UNSUPPORTED, "%s: block_size %d (supported: 16)", fn, block_size);
+  if (cp_size < 1 || cp_rank < 0 || cp_rank >= cp_size)
+    return fail(CPA_ERR_INVALID_ARG, "%s: need 0 <= cp_rank < cp_size (got %d, %d)", fn, cp_rank, cp_size);
+  if (interleave < 1) return fail(CPA_ERR_INVALID_ARG, "%s: interleave %d < 1", fn, interleave);
+  if ((int64_t)interleave * cp_size > INT32_MAX / 2)
+    return fail(CPA_ERR_INVALID_ARG, "%s: interleave * cp_size too large", fn);
+  if (max_blocks < 0) return fail(CPA_ERR_INVALID_ARG, "%s: max_blocks < 0", fn);
+  if (num_seqs > 0 && max_q > 0 && (!block_table || !local_kv_lens) && max_blocks > 0)
+    return fail(CPA_ERR_INVALID_ARG, "%s: block_table or local_kv_lens is NULL", fn);
+  if (num_seqs > 0 && max_q > 0 && !local_kv_lens)
+    return fail(CPA_ERR_INVALID_ARG, "%s: local_kv_lens is NULL", fn);
+  const bool decode = max_q == 1;
+  if (decode) {
+    const size_t need = decode_workspace_bytes(num_seqs, max_blocks, block_size, hq, d);
+    if (workspace_bytes < need)
+      return fail(CPA_ERR_CAPACITY, "%s: workspace has %zu bytes, decode needs %zu", fn, workspace_bytes, need);
+    if (need > 0 && !workspace) return fail(CPA_ERR_INVALID_ARG, "%s: workspace is NULL", fn);
+  }
+  st = check_device();
+  if (st != CPA_OK) return st;
+  if (num_seqs == 0 || max_q == 0) return CPA_OK;
+  AttnArgs a;
+  a.q = q;
+  a.q_pos = q_pos;
+  a.cu_q = cu_q;
+  a.k = k_cache;
+  a.v = v_cache;
+  a.block_table = block_table;
+  a.max_blocks = max_blocks;
+  a.local_kv_lens = local_kv_lens;
+  a.cp = cp_size;
+  a.rank = cp_rank;
+  a.interleave = interleave;
+  a.num_seqs = num_seqs;
+  a.max_q = max_q;
+  a.hq = hq;
+  a.hkv = hkv;
+  a.d = d;
+  a.scale = scale;
+  a.causal = mask == CPA_MASK_CAUSAL;
+  a.o = o;
+  a.o_bf16 = o_dtype == CPA_BF16;
+  a.lse = lse;
+  a.workspace = workspace;
+  a.workspace_bytes = workspace_bytes;
+  hipStream_t s = (hipStream_t)stream;
+  return decode ? launch_attn_decode(a, s) : launch_attn_mfma(a, /*paged=*/true, s);
+}

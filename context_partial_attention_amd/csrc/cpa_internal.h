@@ -1,0 +1,67 @@
+// Internal helpers shared by the library's translation units (not installed).
+#pragma once
+
+#include <cstdarg>
+#include <cstdint>
+#include <cstdio>
+#include <string>
+
+#include <hip/hip_runtime.h>
+
+#include "cpattn.h"
+
+namespace cpa {
+
+// Records a formatted message for cpa_last_error() and returns `s`.
+cpa_status fail(cpa_status s, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+
+// Checks that the current HIP device is gfx950 (cached per device).
+cpa_status check_device();
+
+// Checks hipGetLastError() after a launch and converts it to a status.
+cpa_status check_launch(const char* what);
+
+inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Number of positions in [0, n) that round-robin placement (groups of
+// `interleave` positions dealt to the ranks in turn, starting with rank 0)
+// stores on `rank`: each full cycle of interleave*cp positions gives
+// `interleave` to every rank, and the leftover fills rank 0's group first.
+inline int64_t rr_local_len(int64_t n, int64_t cp, int64_t rank, int64_t interleave) {
+  const int64_t cyc = interleave * cp;
+  int64_t rest = n % cyc - rank * interleave;
+  rest = rest < 0 ? 0 : (rest > interleave ? interleave : rest);
+  return (n / cyc) * interleave + rest;
+}
+
+// Arguments of one partial-attention launch, validated on the host. The
+// contiguous form uses k/v/k_pos/cu_k; the paged form uses k/v as the block
+// caches plus block_table/max_blocks/local_kv_lens/cp/rank/interleave.
+struct AttnArgs {
+  const void* q = nullptr;
+  const int32_t* q_pos = nullptr;
+  const int32_t* cu_q = nullptr;
+  const void* k = nullptr;
+  const void* v = nullptr;
+  const int32_t* k_pos = nullptr;
+  const int32_t* cu_k = nullptr;
+  const int32_t* block_table = nullptr;
+  int32_t max_blocks = 0;
+  const int32_t* local_kv_lens = nullptr;
+  int32_t cp = 1, rank = 0, interleave = 1;
+  int32_t num_seqs = 0, max_q = 0, hq = 0, hkv = 0, d = 0;
+  float scale = 1.f;
+  int causal = 1;
+  void* o = nullptr;
+  bool o_bf16 = false;
+  float* lse = nullptr;
+  void* workspace = nullptr;
+  size_t workspace_bytes = 0;
+};
+
+cpa_status launch_attn_f32(const AttnArgs& a, hipStream_t st);
+cpa_status launch_attn_mfma(const AttnArgs& a, bool paged, hipStream_t st);
+size_t decode_workspace_bytes(int32_t num_seqs, int32_t max_blocks, int32_t block_size, int32_t hq, int32_t d);
+cpa_status launch_attn_decode(const AttnArgs& a, hipStream_t st);
+
+}  // namespace cpa

@@ -1,0 +1,140 @@
+// Host-side integer work of the C ABI: zigzag partition, round-robin
+// placement, error reporting and the device check.
+#include <hip/hip_runtime.h>
+
+#include <climits>
+#include <cstring>
+#include <mutex>
+#include <vector>
+
+#include "cpa_internal.h"
+
+namespace cpa {
+
+static thread_local std::string g_last_error;
+
+cpa_status fail(cpa_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return s;
+}
+
+cpa_status check_device() {
+  static std::mutex mu;
+  static int known[64] = {0};  // 0 unknown, 1 gfx950, -1 other
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(CPA_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= 64) return fail(CPA_ERR_UNSUPPORTED, "device index %d out of range", dev);
+  std::lock_guard<std::mutex> lock(mu);
+  if (known[dev] == 0) {
+    hipDeviceProp_t prop;
+    e = hipGetDeviceProperties(&prop, dev);
+    if (e != hipSuccess) return fail(CPA_ERR_HIP, "hipGetDeviceProperties: %s", hipGetErrorString(e));
+    known[dev] = (std::strncmp(prop.gcnArchName, "gfx950", 6) == 0) ? 1 : -1;
+    if (known[dev] < 0) return fail(CPA_ERR_UNSUPPORTED, "device %d is %s, not gfx950", dev, prop.gcnArchName);
+  }
+  if (known[dev] < 0) return fail(CPA_ERR_UNSUPPORTED, "device %d is not gfx950", dev);
+  return CPA_OK;
+}
+
+cpa_status check_launch(const char* what) {
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(CPA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+  return CPA_OK;
+}
+
+}  // namespace cpa
+
+using cpa::fail;
+
+extern "C" const char* cpa_last_error(void) { return cpa::g_last_error.c_str(); }
+
+// Zigzag split: 2*cp contiguous chunks per sequence (the first L mod 2cp one
+// token longer), rank r owns chunk r and chunk 2cp-1-r, in ascending position.
+extern "C" cpa_status cpa_cp_partition(int32_t num_seqs, const int32_t* seq_lens, int32_t cp_size,
+                                       int32_t rank, int32_t* chunk_bounds, int32_t* cu_seqlens,
+                                       int32_t* positions, int32_t* src_index, int64_t cap,
+                                       int64_t* n_out) {
+  if (!n_out) return fail(CPA_ERR_INVALID_ARG, "cpa_cp_partition: n_out is NULL");
+  if (num_seqs < 0) return fail(CPA_ERR_INVALID_ARG, "cpa_cp_partition: num_seqs < 0");
+  if (num_seqs > 0 && !seq_lens) return fail(CPA_ERR_INVALID_ARG, "cpa_cp_partition: seq_lens is NULL");
+  if (cp_size < 1) return fail(CPA_ERR_INVALID_ARG, "cpa_cp_partition: cp_size %d < 1", cp_size);
+  if (rank < 0 || rank >= cp_size)
+    return fail(CPA_ERR_INVALID_ARG, "cpa_cp_partition: rank %d not in [0, %d)", rank, cp_size);
+  const int64_t n = 2LL * cp_size;
+  int64_t total = 0, all = 0;
+  for (int32_t b = 0; b < num_seqs; ++b) {
+    const int64_t L = seq_lens[b];
+    if (L < 0) return fail(CPA_ERR_INVALID_ARG, "cpa_cp_partition: seq_lens[%d] = %lld < 0", b, (long long)L);
+    const int64_t base = L / n, rem = L % n;
+    const int64_t lo = rank, hi = n - 1 - rank;
+    total += (base + (lo < rem)) + (base + (hi < rem));
+    all += L;
+  }
+  if (all > INT32_MAX) return fail(CPA_ERR_INVALID_ARG, "cpa_cp_partition: total tokens exceed INT32_MAX");
+  *n_out = total;
+  if ((positions || src_index) && total > cap)
+    return fail(CPA_ERR_CAPACITY, "cpa_cp_partition: need %lld output slots, cap is %lld", (long long)total,
+                (long long)cap);
+  int64_t out = 0, seq_start = 0;
+  if (cu_seqlens && num_seqs >= 0) cu_seqlens[0] = 0;
+  for (int32_t b = 0; b < num_seqs; ++b) {
+    const int64_t L = seq_lens[b];
+    const int64_t base = L / n, rem = L % n;
+    // chunk c starts at c*base + min(c, rem)
+    auto start = [&](int64_t c) { return c * base + (c < rem ? c : rem); };
+    if (chunk_bounds)
+      for (int64_t c = 0; c <= n; ++c) chunk_bounds[b * (n + 1) + c] = (int32_t)start(c);
+    const int64_t own[2] = {rank, n - 1 - rank};
+    for (int k = 0; k < 2; ++k) {
+      const int64_t a = start(own[k]), e = start(own[k] + 1);
+      for (int64_t p = a; p < e; ++p, ++out) {
+        if (positions) positions[out] = (int32_t)p;
+        if (src_index) src_index[out] = (int32_t)(seq_start + p);
+      }
+    }
+    if (cu_seqlens) cu_seqlens[b + 1] = (int32_t)out;
+    seq_start += L;
+  }
+  return CPA_OK;
+}
+
+// Round-robin placement with interleave I: position t lives on rank
+// (t / I) mod cp at local slot (t / (I*cp))*I + t mod I.
+extern "C" cpa_status cpa_rr_placement(int32_t num_seqs, const int32_t* seq_lens, int32_t cp_size,
+                                       int32_t rank, int32_t interleave, int32_t* local_lens,
+                                       int32_t* local_to_global, int64_t cap, int64_t* n_out) {
+  if (!n_out) return fail(CPA_ERR_INVALID_ARG, "cpa_rr_placement: n_out is NULL");
+  if (num_seqs < 0) return fail(CPA_ERR_INVALID_ARG, "cpa_rr_placement: num_seqs < 0");
+  if (num_seqs > 0 && (!seq_lens || !local_lens))
+    return fail(CPA_ERR_INVALID_ARG, "cpa_rr_placement: seq_lens or local_lens is NULL");
+  if (cp_size < 1) return fail(CPA_ERR_INVALID_ARG, "cpa_rr_placement: cp_size %d < 1", cp_size);
+  if (rank < 0 || rank >= cp_size)
+    return fail(CPA_ERR_INVALID_ARG, "cpa_rr_placement: rank %d not in [0, %d)", rank, cp_size);
+  if (interleave < 1) return fail(CPA_ERR_INVALID_ARG, "cpa_rr_placement: interleave %d < 1", interleave);
+  int64_t total = 0, all = 0;
+  for (int32_t b = 0; b < num_seqs; ++b) {
+    if (seq_lens[b] < 0) return fail(CPA_ERR_INVALID_ARG, "cpa_rr_placement: seq_lens[%d] < 0", b);
+    total += cpa::rr_local_len(seq_lens[b], cp_size, rank, interleave);
+    all += seq_lens[b];
+  }
+  if (all > INT32_MAX) return fail(CPA_ERR_INVALID_ARG, "cpa_rr_placement: total tokens exceed INT32_MAX");
+  *n_out = total;
+  if (local_to_global && total > cap)
+    return fail(CPA_ERR_CAPACITY, "cpa_rr_placement: need %lld output slots, cap is %lld", (long long)total,
+                (long long)cap);
+  int64_t out = 0;
+  for (int32_t b = 0; b < num_seqs; ++b) {
+    const int64_t n = cpa::rr_local_len(seq_lens[b], cp_size, rank, interleave);
+    local_lens[b] = (int32_t)n;
+    if (local_to_global)
+      for (int64_t l = 0; l < n; ++l, ++out)
+        local_to_global[out] = (int32_t)(((l / interleave) * cp_size + rank) * interleave + l % interleave);
+  }
+  return CPA_OK;
+}

@@ -1,0 +1,216 @@
+/*
+ * cpattn.h — C ABI of libcpattn.so: partial causal GQA attention and exact
+ * log-sum-exp (LSE) merge for context parallelism, on AMD MI355X (gfx950).
+ *
+ * What is computed comes from three vLLM pull-request pages:
+ *   [PCP-GQA]  "[Feature] Support Prefill Context Parallel (PCP) for GQA flashinfer"
+ *   [PASSKV]   "Add utility functions to enable pass-kv prefill and allgather decode"
+ *   [PCP-BASE] "[Feature] Prefill Context Parallel (PCP) basic support"
+ * Context parallelism (CP) shards a sequence over cp ranks. Attention is the
+ * only sequence-coupled operation ([PASSKV], Purpose), so a rank's queries
+ * attend to one KV shard at a time ("partial attention"), each step giving a
+ * partial output O and its LSE, and the partials are merged exactly.
+ *
+ * Conventions (all entry points):
+ *  - Every call returns cpa_status: 0 on success, a negative code on error.
+ *    cpa_last_error() then returns a message (thread-local, valid until the
+ *    next failing call on the same thread). No exception crosses the ABI.
+ *  - Ownership: the caller allocates every buffer. Host calls read and write
+ *    caller host arrays synchronously. Device calls take device pointers,
+ *    validate every host-side argument before touching the GPU, enqueue their
+ *    kernels on `stream` (a hipStream_t; NULL is the default stream) and
+ *    return without synchronising. Errors the GPU could only report later
+ *    (an out-of-range block-table entry, say) are not detected.
+ *  - The library allocates no device memory. Scratch space, where a call
+ *    needs any, is a caller-supplied workspace whose size is queried first.
+ *  - Layouts are row-major and token-major:
+ *      q, o      [T][hq][d]          k, v   [T][hkv][d]
+ *      lse       [T][hq]             paged k/v cache [num_blocks][hkv][block_size][d]
+ *    Query head h reads KV head h / (hq / hkv) (contiguous GQA groups).
+ *  - LSE is the natural logarithm of the sum over visible keys of
+ *    exp(scale * <q, k>). A row that sees no key has O = 0 and LSE = -inf.
+ *  - Positions are global token positions within a sequence and must be
+ *    non-decreasing within each sequence (zigzag shards and round-robin
+ *    local orders are). The kernels use this to skip masked tiles.
+ *  - Device calls run on gfx950 only; any other device gives
+ *    CPA_ERR_UNSUPPORTED.
+ */
+#ifndef CPATTN_H
+#define CPATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  CPA_OK = 0,
+  CPA_ERR_INVALID_ARG = -1, /* bad pointer, size, shape or enum value */
+  CPA_ERR_UNSUPPORTED = -2, /* valid but not implemented (d, dtype, device) */
+  CPA_ERR_CAPACITY = -3,    /* an output or workspace is too small */
+  CPA_ERR_HIP = -4          /* the HIP runtime reported an error */
+} cpa_status;
+
+typedef enum { CPA_BF16 = 0, CPA_F32 = 1 } cpa_dtype;
+
+/* CPA_MASK_CAUSAL: query i sees key j iff k_pos[j] <= q_pos[i] (global
+ * positions). The offset-causal mask of chunked prefill is this mask with the
+ * new queries' positions starting at the cached length.
+ * CPA_MASK_NONE: every query sees every key of its sequence's shard. */
+typedef enum { CPA_MASK_NONE = 0, CPA_MASK_CAUSAL = 1 } cpa_mask;
+
+/* Message for the last failing call on this thread ("" if none). */
+const char* cpa_last_error(void);
+
+/* ---------------------------------------------------------------------------
+ * cpa_cp_partition — the query/KV shard one CP rank holds at prefill (host).
+ *
+ * [PCP-GQA] and [PCP-BASE], Purpose: prefill CP partitions the sequence
+ * dimension across ranks. Each sequence of length L is cut into 2*cp
+ * contiguous chunks (sizes floor(L/2cp), the first L mod 2cp chunks one
+ * larger) and rank r owns chunk r and chunk 2cp-1-r, the zigzag pairing that
+ * gives every rank the same number of causal pairs when 2cp divides L.
+ * A shard lists its tokens in ascending position; shards of a batch are
+ * packed sequence after sequence.
+ *
+ * In:  num_seqs >= 0; seq_lens[num_seqs] >= 0 (host); cp_size >= 1;
+ *      0 <= rank < cp_size.
+ * Out (host arrays, caller-allocated):
+ *      chunk_bounds [num_seqs][2*cp_size+1] chunk starts then L (may be NULL)
+ *      cu_seqlens   [num_seqs+1]            shard offsets          (may be NULL)
+ *      positions    [cap] global position of each shard token      (may be NULL)
+ *      src_index    [cap] index of the token in the packed unsharded batch
+ *                         (may be NULL)
+ *      *n_out = total shard tokens (required, never NULL).
+ * Size query: with positions == src_index == NULL, only *n_out (and the
+ * non-NULL small arrays) are written. CPA_ERR_CAPACITY if n_out > cap while
+ * positions or src_index is non-NULL; nothing is then written to them.
+ * Errors: CPA_ERR_INVALID_ARG on NULL seq_lens with num_seqs > 0, negative
+ * lengths, cp_size < 1, rank out of range, or totals above INT32_MAX.
+ * ------------------------------------------------------------------------- */
+cpa_status cpa_cp_partition(int32_t num_seqs, const int32_t* seq_lens, int32_t cp_size,
+                            int32_t rank, int32_t* chunk_bounds, int32_t* cu_seqlens,
+                            int32_t* positions, int32_t* src_index, int64_t cap,
+                            int64_t* n_out);
+
+/* ---------------------------------------------------------------------------
+ * cpa_rr_placement — round-robin KV placement with an interleave size (host).
+ *
+ * [PASSKV], Purpose: for decode the KV cache is stored on the CP ranks in a
+ * round-robin manner; [PCP-GQA], Test Plan, and [PCP-BASE], review summary:
+ * the placement has an interleave size shared by prefill and decode CP.
+ * Position t is stored on rank (t / I) mod cp at local slot
+ * (t / (I*cp))*I + t mod I; positions [0, I) go to rank 0.
+ *
+ * In:  num_seqs >= 0; seq_lens[num_seqs] (host); cp_size >= 1;
+ *      0 <= rank < cp_size; interleave I >= 1.
+ * Out: local_lens[num_seqs] (required); local_to_global[cap] the global
+ *      position of each local slot, packed sequence after sequence (may be
+ *      NULL); *n_out = sum(local_lens) (required).
+ * Errors: as cpa_cp_partition; CPA_ERR_INVALID_ARG also for interleave < 1.
+ * ------------------------------------------------------------------------- */
+cpa_status cpa_rr_placement(int32_t num_seqs, const int32_t* seq_lens, int32_t cp_size,
+                            int32_t rank, int32_t interleave, int32_t* local_lens,
+                            int32_t* local_to_global, int64_t cap, int64_t* n_out);
+
+/* ---------------------------------------------------------------------------
+ * cpa_partial_attn — one pass-KV step: a packed Q shard against one packed,
+ * contiguous KV shard, giving partial O and LSE (device).
+ *
+ * [PASSKV], Purpose: Q and KV are both sharded at prefill; each step of the
+ * exchange computes a partial attention of the local queries against one
+ * KV shard, and the partials are merged (cpa_lse_merge).
+ *
+ * In (device pointers):
+ *   q      [Tq][hq][d]   in_dtype          q_pos [Tq] int32, cu_q [num_seqs+1] int32
+ *   k, v   [Tk][hkv][d]  in_dtype          k_pos [Tk] int32, cu_k [num_seqs+1] int32
+ *   Sequence b's queries are rows cu_q[b]..cu_q[b+1]-1 and its keys rows
+ *   cu_k[b]..cu_k[b+1]-1; q_pos and k_pos must be non-decreasing within a
+ *   sequence.
+ * In (host values): num_seqs >= 1; max_q >= max_b(cu_q[b+1]-cu_q[b]);
+ *   hq % hkv == 0; d in {64, 128}; in_dtype CPA_BF16 or CPA_F32; scale > 0
+ *   (normally 1/sqrt(d)); mask.
+ * Out (device): o [Tq][hq][d] in o_dtype (CPA_F32, or CPA_BF16 when
+ *   in_dtype is CPA_BF16); lse [Tq][hq] float.
+ * The caller guarantees max_q; rows beyond it are not computed.
+ * Errors: CPA_ERR_INVALID_ARG (NULL pointer, bad sizes), CPA_ERR_UNSUPPORTED
+ *   (d, dtype combination, device), CPA_ERR_HIP (launch failure).
+ * ------------------------------------------------------------------------- */
+cpa_status cpa_partial_attn(const void* q, const int32_t* q_pos, const int32_t* cu_q,
+                            const void* k, const void* v, const int32_t* k_pos,
+                            const int32_t* cu_k, int32_t num_seqs, int32_t max_q, int32_t hq,
+                            int32_t hkv, int32_t d, cpa_dtype in_dtype, float scale,
+                            cpa_mask mask, void* o, cpa_dtype o_dtype, float* lse,
+                            void* stream);
+
+/* ---------------------------------------------------------------------------
+ * cpa_partial_attn_paged_workspace — bytes of device workspace that
+ * cpa_partial_attn_paged needs for these sizes (host, no GPU access).
+ * Zero when no workspace is needed (max_q > 1).
+ * ------------------------------------------------------------------------- */
+cpa_status cpa_partial_attn_paged_workspace(int32_t num_seqs, int32_t max_q,
+                                            int32_t max_blocks, int32_t block_size,
+                                            int32_t hq, int32_t d, size_t* bytes);
+
+/* ---------------------------------------------------------------------------
+ * cpa_partial_attn_paged — partial attention against one rank's paged,
+ * round-robin-placed KV shard (device).
+ *
+ * [PASSKV], Purpose: for chunked prefill, passing Q is preferred when the KV
+ * cache is much longer than the new tokens, so every rank attends the visiting
+ * queries to its resident KV; for decode, Q is all-gathered and each rank
+ * attends to its round-robin share of the cache. [PCP-BASE], Purpose: the
+ * KV-cache block tables are extended for CP. Local slot l of sequence b is
+ * at physical block block_table[b][l / block_size], row l mod block_size,
+ * and holds global position ((l / I)*cp_size + cp_rank)*I + l mod I.
+ * max_q > 1 selects the prefill kernel (pass-Q, offset-causal mask);
+ * max_q == 1 selects the split-KV decode kernel, which needs the workspace.
+ *
+ * In (device): q [Tq][hq][d], q_pos [Tq], cu_q [num_seqs+1] as in
+ *   cpa_partial_attn; k_cache, v_cache [num_blocks][hkv][block_size][d];
+ *   block_table [num_seqs][max_blocks] int32; local_kv_lens [num_seqs] int32
+ *   with local_kv_lens[b] <= max_blocks*block_size.
+ * In (host): block_size == 16; cp_size >= 1; 0 <= cp_rank < cp_size;
+ *   interleave >= 1; d in {64, 128}; in_dtype CPA_BF16; hq % hkv == 0.
+ * Out (device): o [Tq][hq][d] (o_dtype CPA_F32 or CPA_BF16), lse [Tq][hq].
+ * workspace: device memory of at least the queried size (may be NULL when
+ *   the query returned 0); contents on return are unspecified.
+ * Errors: as cpa_partial_attn; CPA_ERR_CAPACITY if workspace_bytes is short.
+ * ------------------------------------------------------------------------- */
+cpa_status cpa_partial_attn_paged(const void* q, const int32_t* q_pos, const int32_t* cu_q,
+                                  const void* k_cache, const void* v_cache,
+                                  const int32_t* block_table, int32_t max_blocks,
+                                  const int32_t* local_kv_lens, int32_t block_size,
+                                  int32_t cp_size, int32_t cp_rank, int32_t interleave,
+                                  int32_t num_seqs, int32_t max_q, int32_t hq, int32_t hkv,
+                                  int32_t d, cpa_dtype in_dtype, float scale, cpa_mask mask,
+                                  void* o, cpa_dtype o_dtype, float* lse, void* workspace,
+                                  size_t workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * cpa_lse_merge — exact n-way merge of partial (O, LSE) results (device).
+ *
+ * The partials come from disjoint key sets (the KV shards of the ranks), so
+ * with M = max_s LSE_s, LSE = M + log sum_s exp(LSE_s - M) and
+ * O = sum_s exp(LSE_s - LSE) O_s equals attention over the union of the key
+ * sets ([PASSKV], Purpose: partial attention over exchanged shards). Rows
+ * whose partials are all -inf give O = 0, LSE = -inf.
+ *
+ * In: n_parts in [1, 16]; o_parts and lse_parts are HOST arrays of n_parts
+ *   DEVICE pointers: o_parts[s] [rows][d] in part_dtype, lse_parts[s]
+ *   [rows] float; rows = tokens * hq >= 0; d in {64, 128}.
+ * Out (device): o_out [rows][d] in out_dtype; lse_out [rows] (may be NULL).
+ * Outputs may alias part 0 only when part_dtype == out_dtype.
+ * ------------------------------------------------------------------------- */
+cpa_status cpa_lse_merge(int32_t n_parts, const void* const* o_parts,
+                         const float* const* lse_parts, cpa_dtype part_dtype, int64_t rows,
+                         int32_t d, void* o_out, cpa_dtype out_dtype, float* lse_out,
+                         void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CPATTN_H */

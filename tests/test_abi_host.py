@@ -1,0 +1,150 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function
+include/cpattn.h declares, its host integer calls match the oracle bit for
+bit, and bad arguments come back as error statuses (before any GPU access).
+"""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def cpa():
+    import context_partial_attention_amd as cpa
+
+    if not os.path.exists(cpa.library_path()):
+        pytest.fail("libcpattn.so is not built (python -m context_partial_attention_amd.build)")
+    cpa.load_library()
+    return cpa
+
+
+def _declared_functions():
+    src = open(os.path.join(ROOT, "include", "cpattn.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(cpa_[a-z_0-9]+)\s*\(", src)))
+
+
+def test_header_declares_the_boundary():
+    names = _declared_functions()
+    for want in ["cpa_cp_partition", "cpa_rr_placement", "cpa_partial_attn", "cpa_partial_attn_paged",
+                 "cpa_partial_attn_paged_workspace", "cpa_lse_merge", "cpa_last_error"]:
+        assert want in names
+
+
+def test_library_exports_every_declared_symbol(cpa):
+    lib = ctypes.CDLL(cpa.library_path())
+    missing = [n for n in _declared_functions() if not hasattr(lib, n)]
+    assert not missing, missing
+
+
+@pytest.mark.parametrize("cp", [1, 2, 3, 4, 8])
+def test_cp_partition_matches_oracle(cpa, cp):
+    rng = np.random.default_rng(cp)
+    lens = [0, 1, 2 * cp - 1, 2 * cp] + rng.integers(0, 5000, size=6).tolist() + [8195, 2051]
+    for r in range(cp):
+        got = cpa.cp_partition(lens, cp, r)
+        want = oracle.zigzag_partition(lens, cp, r)
+        for key in ("chunk_bounds", "cu_seqlens", "positions", "src_index"):
+            np.testing.assert_array_equal(got[key], want[key].astype(np.int32), err_msg=key)
+
+
+@pytest.mark.parametrize("cp,I", [(1, 1), (2, 8), (3, 2), (4, 8), (4, 16), (8, 1)])
+def test_rr_placement_matches_oracle(cpa, cp, I):
+    rng = np.random.default_rng(cp * 10 + I)
+    lens = [0, 1, I, I * cp, I * cp + 1] + rng.integers(0, 3000, size=6).tolist()
+    for r in range(cp):
+        got = cpa.rr_placement(lens, cp, r, I)
+        want = oracle.rr_placement(lens, cp, r, I)
+        np.testing.assert_array_equal(got["local_lens"], want["local_lens"].astype(np.int32))
+        np.testing.assert_array_equal(got["local_to_global"], want["local_to_global"].astype(np.int32))
+
+
+def test_workload_sized_placement(cpa):
+    # the chunked-prefill layout: 69632 tokens over 4 ranks, interleave 8
+    for r in range(4):
+        got = cpa.rr_placement([69632, 69632], 4, r, 8)
+        assert got["local_lens"].tolist() == [17408, 17408]
+        want = oracle.rr_placement([69632], 4, r, 8)["local_to_global"].astype(np.int32)
+        np.testing.assert_array_equal(got["local_to_global"][:17408], want)
+
+
+def test_partition_large_sequence(cpa):
+    got = cpa.cp_partition([131072], 4, 1)
+    assert got["positions"][0] == 16384 and got["positions"][16383] == 32767
+    assert got["positions"][16384] == 98304 and got["positions"][-1] == 114687
+
+
+def _status(fn, *args):
+    return fn(*args)
+
+
+def test_host_error_statuses(cpa):
+    lib = cpa.load_library()
+    n = ctypes.c_int64(0)
+    lens = (ctypes.c_int32 * 2)(10, 20)
+    # rank out of range, cp < 1, NULL n_out, negative length, capacity too small
+    assert lib.cpa_cp_partition(2, lens, 2, 2, None, None, None, None, 0, ctypes.byref(n)) == -1
+    assert b"rank" in lib.cpa_last_error()
+    assert lib.cpa_cp_partition(2, lens, 0, 0, None, None, None, None, 0, ctypes.byref(n)) == -1
+    assert lib.cpa_cp_partition(2, lens, 2, 0, None, None, None, None, 0, None) == -1
+    bad = (ctypes.c_int32 * 1)(-5)
+    assert lib.cpa_cp_partition(1, bad, 2, 0, None, None, None, None, 0, ctypes.byref(n)) == -1
+    small = (ctypes.c_int32 * 4)()
+    assert lib.cpa_cp_partition(2, lens, 2, 0, None, None, small, None, 4, ctypes.byref(n)) == -3
+    assert n.value == 15
+    loc = (ctypes.c_int32 * 2)()
+    assert lib.cpa_rr_placement(2, lens, 2, 0, 0, loc, None, 0, ctypes.byref(n)) == -1  # interleave 0
+    assert lib.cpa_rr_placement(2, lens, 2, 0, 8, loc, small, 4, ctypes.byref(n)) == -3
+    # rank 0 at cp=2, I=8 holds positions 0-7 of L=10 and 0-7, 16-19 of L=20: 8 + 12 tokens
+    assert lib.cpa_rr_placement(2, lens, 2, 0, 8, loc, None, 0, ctypes.byref(n)) == 0 and n.value == 20
+    assert list(loc) == [8, 12]
+
+
+def test_device_call_validation_before_gpu(cpa):
+    """Argument errors are reported without touching a GPU (none is present here)."""
+    lib = cpa.load_library()
+    fake = ctypes.c_void_p(0x1000)  # never dereferenced: validation fails first
+    # hq not a multiple of hkv
+    assert lib.cpa_partial_attn(fake, fake, fake, fake, fake, fake, fake, 1, 4, 6, 4, 128, 0, 0.1, 1, fake, 1,
+                                fake, None) == -1
+    # unsupported head dim
+    assert lib.cpa_partial_attn(fake, fake, fake, fake, fake, fake, fake, 1, 4, 8, 2, 96, 0, 0.1, 1, fake, 1,
+                                fake, None) == -2
+    # fp32 input with bf16 output
+    assert lib.cpa_partial_attn(fake, fake, fake, fake, fake, fake, fake, 1, 4, 8, 2, 64, 1, 0.1, 1, fake, 0,
+                                fake, None) == -2
+    # bad scale, bad mask
+    assert lib.cpa_partial_attn(fake, fake, fake, fake, fake, fake, fake, 1, 4, 8, 2, 64, 0, -1.0, 1, fake, 1,
+                                fake, None) == -1
+    assert lib.cpa_partial_attn(fake, fake, fake, fake, fake, fake, fake, 1, 4, 8, 2, 64, 0, 0.1, 7, fake, 1,
+                                fake, None) == -1
+    # NULL output pointer
+    assert lib.cpa_partial_attn(fake, fake, fake, fake, fake, fake, fake, 1, 4, 8, 2, 64, 0, 0.1, 1, None, 1,
+                                fake, None) == -1
+    # paged: cp_rank >= cp_size, interleave 0, block size 32, workspace too small for decode
+    args = dict(bs=16, cp=2, rank=0, il=8, maxq=4, ws=None, wsb=0)
+
+    def paged(bs=16, cp=2, rank=0, il=8, maxq=4, ws=None, wsb=0, dtype=0):
+        return lib.cpa_partial_attn_paged(fake, fake, fake, fake, fake, fake, 8, fake, bs, cp, rank, il, 2, maxq,
+                                          8, 2, 128, dtype, 0.1, 1, fake, 1, fake, ws, wsb, None)
+
+    assert paged(**{**args, "rank": 2}) == -1
+    assert paged(**{**args, "il": 0}) == -1
+    assert paged(**{**args, "bs": 32}) == -2
+    assert paged(**{**args, "maxq": 1}) == -3
+    assert paged(dtype=1) == -2
+    need = ctypes.c_size_t(0)
+    assert lib.cpa_partial_attn_paged_workspace(2, 1, 8, 16, 8, 128, ctypes.byref(need)) == 0
+    assert need.value == 2 * 8 * 1 * 129 * 4
+    assert lib.cpa_partial_attn_paged_workspace(2, 7, 8, 16, 8, 128, ctypes.byref(need)) == 0 and need.value == 0
+    # merge: too many parts, bad d
+    ptrs = (ctypes.c_void_p * 17)(*([0x1000] * 17))
+    assert lib.cpa_lse_merge(17, ptrs, ptrs, 1, 10, 128, fake, 1, fake, None) == -1
+    assert lib.cpa_lse_merge(2, ptrs, ptrs, 1, 10, 80, fake, 1, fake, None) == -2
+    assert lib.cpa_lse_merge(0, ptrs, ptrs, 1, 10, 128, fake, 1, fake, None) == -1

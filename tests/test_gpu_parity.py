@@ -1,0 +1,250 @@
+"""GPU parity: every entry point of libcpattn.so against the fp64 CPU oracle.
+
+Small cases compare every output element; the full-size workloads (run in the
+same launch configuration the benchmark times) compare sampled rows against
+the oracle and check properties that hold at any size on every row. The bar:
+max |dO| <= 2e-2 and max |dLSE| <= 1e-3 for bf16 inputs with fp32
+accumulation, rows with no visible key exactly (O = 0, LSE = -inf), no NaN.
+"""
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from parity_util import (assert_close, expected_pass_kv, expected_round_robin, f64, sample_rows)
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def cpa(gpu):
+    import context_partial_attention_amd as cpa
+
+    cpa.load_library()
+    return cpa
+
+
+@pytest.fixture(scope="module")
+def wl():
+    from context_partial_attention_amd import workloads
+
+    return workloads
+
+
+@pytest.fixture(scope="module")
+def harness():
+    from context_partial_attention_amd import harness
+
+    return harness
+
+
+def _check_schedule(harness, w, rows=None, pool_fill=0.0, seed=0):
+    """Runs a workload's whole schedule on the GPU and compares every partial
+    and the merge with the oracle on `rows` (all rows when None)."""
+    inp = harness.build(w, device="cuda", pool_fill=pool_fill)
+    run = harness.Runner(inp)
+    run.step()
+    torch.cuda.synchronize()
+    if w.kind == "pass_kv":
+        rows_, parts, merged = expected_pass_kv(inp, rows)
+    else:
+        rows_, parts, merged = expected_round_robin(inp, rows)
+    ridx = torch.as_tensor(rows_, device="cuda")
+    errs = []
+    for s, (o_ref, l_ref) in enumerate(parts):
+        errs.append(assert_close(f64(run.o_parts[s][ridx]), f64(run.lse_parts[s][ridx]), o_ref, l_ref,
+                                 f"{w.name} partial {s}"))
+    errs.append(assert_close(f64(run.o[ridx]), f64(run.lse[ridx]), merged[0], merged[1], f"{w.name} merged"))
+    return inp, run, errs
+
+
+# ----------------------------------------------------------------- tiny fp32 workload, every element
+
+
+def test_tiny_prefill_cp2_fp32_all_elements(cpa, wl, harness):
+    w = wl.WORKLOADS["tiny_prefill_cp2"]
+    _say(f"case {w.name}")
+    inp, run, errs = _check_schedule(harness, w)
+    # fp32 inputs: the merged result must also equal full causal attention of the sequence
+    q = f64(inp["draws"][0][0])
+    k = f64(inp["draws"][0][1])
+    v = f64(inp["draws"][0][2])
+    fo, fl = oracle.full_causal_attn(q, k, v, w.scale, rows=inp["q_positions_host"])
+    assert_close(f64(run.o), f64(run.lse), fo, fl, "tiny merged vs full attention", o_tol=1e-4, lse_tol=1e-5)
+    # chunk-0 queries see nothing of rank 1's shard in step 2
+    assert np.all(np.isneginf(f64(run.lse_parts[1])[:64]))
+
+
+# ----------------------------------------------------------------- small bf16 variants, every element
+
+
+SMALL = [
+    # name, kind, changes
+    ("passkv_ragged_cp2_r0", dict(kind="pass_kv", lengths=(300, 517, 1000), batch=3, len_range=(), cp=2, rank=0)),
+    ("passkv_ragged_cp2_r1", dict(kind="pass_kv", lengths=(300, 517, 1000), batch=3, len_range=(), cp=2, rank=1)),
+    ("passkv_cp4_r3_d64_g1", dict(kind="pass_kv", lengths=(777,), batch=1, len_range=(), cp=4, rank=3, hq=4, hkv=4,
+                                  d=64)),
+    ("passkv_tiny_chunks", dict(kind="pass_kv", lengths=(3, 1, 0, 9, 130), batch=5, len_range=(), cp=4, rank=2)),
+    ("passq_cp4_small", dict(kind="pass_q", batch=2, cached=1000, new=300, cp=4, rank=0, interleave=8)),
+    ("passq_cp3_il5_d64", dict(kind="pass_q", batch=3, cached=513, new=130, cp=3, rank=0, interleave=5, d=64,
+                               hq=8, hkv=1)),
+    ("decode_cp2_small", dict(kind="decode", batch=16, len_range=(1, 3000), lengths=(), cp=2, rank=0,
+                              interleave=8)),
+    ("decode_cp4_d64_g8", dict(kind="decode", batch=9, len_range=(1, 700), lengths=(), cp=4, rank=0, interleave=3,
+                               d=64, hq=16, hkv=2)),
+]
+
+
+@pytest.mark.parametrize("name,changes", SMALL, ids=[s[0] for s in SMALL])
+def test_small_bf16_all_elements(cpa, wl, harness, name, changes):
+    base = {"pass_kv": "qwen2.5_3b_cp2_rank0", "pass_q": "chunked_prefill_passq_cp4",
+            "decode": "allgather_decode_cp2"}[changes["kind"]]
+    w = wl.scaled(wl.WORKLOADS[base], name=name, seed=100 + len(name), **changes)
+    _say(f"case {name}")
+    # NaN in every unused cache slot: any read of one would show up in the results
+    _check_schedule(harness, w, pool_fill=float("nan"))
+
+
+def test_small_bf16_output_and_no_mask(cpa, wl, harness):
+    w = wl.scaled(wl.WORKLOADS["qwen2.5_3b_cp2_rank0"], name="nomask", lengths=(400, 129), batch=2, len_range=())
+    _say("case bf16 output + no mask")
+    inp = harness.build(w, device="cuda")
+    st = inp["steps"][1]
+    o, l = cpa.partial_attn(inp["q"], inp["q_pos"], inp["cu_q"], st["k"], st["v"], st["k_pos"], st["cu_k"],
+                            inp["max_q"], w.scale, causal=False, out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    mine = oracle.zigzag_partition(inp["lens"], w.cp, w.rank)
+    src = oracle.zigzag_partition(inp["lens"], w.cp, (w.rank - 1) % w.cp)
+    q_all = torch.cat([d[0] for d in inp["draws"]])
+    k_all = torch.cat([d[1] for d in inp["draws"]])
+    v_all = torch.cat([d[2] for d in inp["draws"]])
+    q = f64(q_all[torch.as_tensor(mine["src_index"], device="cuda")])
+    k = f64(k_all[torch.as_tensor(src["src_index"], device="cuda")])
+    v = f64(v_all[torch.as_tensor(src["src_index"], device="cuda")])
+    ro, rl = oracle.partial_attn(q, mine["positions"], mine["cu_seqlens"], k, v, src["positions"],
+                                 src["cu_seqlens"], w.scale, causal=False)
+    assert_close(f64(o), f64(l), ro, rl, "no-mask bf16-out")
+
+
+def test_invariants_ones_and_zero_keys(cpa, wl, harness):
+    """V = 1 gives O = 1 on every row that sees a key; K = 0 gives
+    LSE = ln(#visible keys) exactly enough to check the mask counts."""
+    w = wl.scaled(wl.WORKLOADS["qwen2.5_3b_cp2_rank0"], name="inv", lengths=(1000, 333), batch=2, len_range=())
+    _say("case invariants")
+    inp = harness.build(w, device="cuda")
+    st = inp["steps"][0]
+    ones = torch.ones_like(st["v"])
+    zeros = torch.zeros_like(st["k"])
+    o, l = cpa.partial_attn(inp["q"], inp["q_pos"], inp["cu_q"], st["k"], ones, st["k_pos"], st["cu_k"],
+                            inp["max_q"], w.scale)
+    o2, l2 = cpa.partial_attn(inp["q"], inp["q_pos"], inp["cu_q"], zeros, st["v"], st["k_pos"], st["cu_k"],
+                              inp["max_q"], w.scale)
+    torch.cuda.synchronize()
+    fin = torch.isfinite(l)
+    # P enters the P.V product rounded to bf16 (relative error <= 2^-9 per weight)
+    # while the normaliser sums fp32 P, so O = 1 holds to within 2^-9 / (1 - 2^-9).
+    assert float(torch.abs(o[fin] - 1).max()) <= 2.0 ** -8
+    qp, cu = inp["q_positions_host"], inp["cu_q_host"]
+    kp, cuk = st["k_positions_host"], st["cu_k_host"]
+    counts = np.zeros(len(qp))
+    for b in range(len(cu) - 1):
+        counts[cu[b]:cu[b + 1]] = np.searchsorted(kp[cuk[b]:cuk[b + 1]], qp[cu[b]:cu[b + 1]], side="right")
+    want = np.where(counts > 0, np.log(np.maximum(counts, 1)), -np.inf)
+    got = f64(l2)
+    for h in range(w.hq):
+        np.testing.assert_array_equal(np.isneginf(got[:, h]), np.isneginf(want))
+        fin = np.isfinite(want)
+        assert np.max(np.abs(got[fin, h] - want[fin])) < 1e-5
+
+
+def test_merge_identity_and_empty_part(cpa):
+    _say("case merge identity")
+    g = torch.Generator(device="cuda").manual_seed(7)
+    o = torch.randn((1000, 8, 128), generator=g, device="cuda")
+    l = torch.randn((1000, 8), generator=g, device="cuda")
+    mo, ml = cpa.lse_merge([o], [l])
+    torch.cuda.synchronize()
+    assert torch.allclose(mo, o, atol=1e-5) and torch.allclose(ml, l, atol=1e-5)
+    mo, ml = cpa.lse_merge([torch.zeros_like(o), o], [torch.full_like(l, -math.inf), l])
+    torch.cuda.synchronize()
+    assert torch.allclose(mo, o, atol=1e-5) and torch.allclose(ml, l, atol=1e-5)
+    e = torch.full_like(l, -math.inf)
+    mo, ml = cpa.lse_merge([torch.zeros_like(o)] * 3, [e] * 3, out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    assert torch.all(torch.isneginf(ml)) and torch.all(mo == 0)
+
+
+@pytest.mark.parametrize("n_parts,d", [(1, 64), (3, 128), (16, 64), (5, 128)])
+def test_merge_random_parts_vs_oracle(cpa, n_parts, d):
+    _say(f"case merge n={n_parts} d={d}")
+    g = torch.Generator(device="cuda").manual_seed(n_parts * 100 + d)
+    rows = 777
+    os_ = [torch.randn((rows, d), generator=g, device="cuda") for _ in range(n_parts)]
+    ls_ = [torch.randn((rows,), generator=g, device="cuda") * 5 for _ in range(n_parts)]
+    ls_[0][::7] = -math.inf
+    for dt in (torch.float32, torch.bfloat16):
+        parts_o = [x.to(dt) for x in os_]
+        mo, ml = cpa.lse_merge(parts_o, ls_, out_dtype=dt)
+        torch.cuda.synchronize()
+        ro, rl = oracle.lse_merge([f64(x) for x in parts_o], [f64(x) for x in ls_])
+        assert_close(f64(mo), f64(ml), ro, rl, f"merge {dt}")
+
+
+# ----------------------------------------------------------------- the five full-size workloads
+
+
+def _row_properties(inp, run):
+    """Properties every row must satisfy at any size: no NaN, merged LSE finite
+    (every query sees at least one key overall), and |O| <= max |V| since O is
+    a convex combination of value rows."""
+    for t in [run.o, run.lse] + run.o_parts + run.lse_parts:
+        assert not torch.isnan(t).any()
+    assert torch.isfinite(run.lse).all()
+    vmax = max(float(d[2].float().abs().max()) for d in inp["draws"])
+    assert float(run.o.float().abs().max()) <= vmax * (1 + 2 ** -8) + 1e-3
+    for o in run.o_parts:
+        assert float(o.abs().max()) <= vmax * (1 + 2 ** -8) + 1e-3
+
+
+@pytest.mark.parametrize("name", ["qwen2.5_3b_cp2_rank0", "llama3_8b_128k_cp4_rank1", "chunked_prefill_passq_cp4",
+                                  "allgather_decode_cp2"])
+def test_full_size_workload_sampled(cpa, wl, harness, name):
+    w = wl.WORKLOADS[name]
+    _say(f"case full-size {name}")
+    inp = harness.build(w, device="cuda")
+    run = harness.Runner(inp)
+    run.step()
+    torch.cuda.synchronize()
+    _row_properties(inp, run)
+    cu, pos = inp["cu_q_host"], inp["q_positions_host"]
+    if w.kind == "decode":
+        rows = np.arange(0, len(pos), 37)  # a spread of sequences, lengths 8K..32K
+    else:
+        rows = sample_rows(cu, pos, n_random=48, seed=w.seed)
+    if w.kind == "pass_kv":
+        rows_, parts, merged = expected_pass_kv(inp, rows)
+        # exact -inf pattern on every row of every step, from positions alone
+        for s, st in enumerate(inp["steps"]):
+            kp, cuk = st["k_positions_host"], st["cu_k_host"]
+            got = f64(run.lse_parts[s])
+            for b in range(len(cu) - 1):
+                qa, qe = cu[b], cu[b + 1]
+                first = kp[cuk[b]] if cuk[b + 1] > cuk[b] else np.iinfo(np.int64).max
+                empty = pos[qa:qe] < first
+                np.testing.assert_array_equal(np.isneginf(got[qa:qe]).all(axis=1), empty)
+    else:
+        rows_, parts, merged = expected_round_robin(inp, rows)
+    ridx = torch.as_tensor(rows_, device="cuda")
+    for s, (o_ref, l_ref) in enumerate(parts):
+        e = assert_close(f64(run.o_parts[s][ridx]), f64(run.lse_parts[s][ridx]), o_ref, l_ref, f"{name} part {s}")
+        _say(f"  part {s}: max|dO|={e[0]:.2e} max|dLSE|={e[1]:.2e} over {len(rows_)} rows")
+    e = assert_close(f64(run.o[ridx]), f64(run.lse[ridx]), merged[0], merged[1], f"{name} merged")
+    _say(f"  merged: max|dO|={e[0]:.2e} max|dLSE|={e[1]:.2e}")
