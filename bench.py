@@ -1,0 +1,343 @@
+"""Throughput of the partial-attention + LSE-merge hot path on one MI355X.
+
+python bench.py [--gpus 1] [--steps K] [--warmup W] [--workloads a,b,...] [--no-cpu-baseline]
+
+A step is one CP rank's whole share of one batch: every partial attention the
+rank computes, then the merge of all partials (other ranks' partials already
+resident in HBM where the schedule has them). Inputs are seeded synthetic
+tensors resident in HBM before timing starts.
+
+Headline (`value`): the Qwen2.5-3B-shaped cp=2 rank-0 pass-KV workload
+(4 sequences of 2048..8192 tokens, 16/2 heads, d=128, bf16): algorithmic
+TFLOP/s = 4 * d * hq * (visible causal pairs) / step time. The other
+full-size workloads are reported under "workloads" (TFLOP/s for prefill,
+GB/s for decode and for every merge).
+
+Prints one JSON line on stdout; progress goes to stderr.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import platform
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "partial-attn+merge TFLOP/s and % bf16 MFMA peak (prefill); GB/s (decode)"
+HEADLINE = "qwen2.5_3b_cp2_rank0"
+DEFAULT_WORKLOADS = [HEADLINE, "llama3_8b_128k_cp4_rank1", "chunked_prefill_passq_cp4", "allgather_decode_cp2"]
+PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0  # MI355X HBM3E
+ATTN_SOURCE = os.path.join(ROOT, "context_partial_attention_amd", "csrc", "attn_mfma.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_mfma_qwen2.5_3b_cp2_traffic.md")
+
+
+def log(msg: str):
+    print(msg, file=sys.stderr, flush=True)
+
+
+# ------------------------------------------------------------------ work counts (host integers)
+
+
+def pass_kv_pairs(inp, step: int) -> int:
+    """Visible (query, key) pairs of one pass-KV step: per query, the keys of
+    its sequence's shard with position <= its own."""
+    qp, cu = inp["q_positions_host"], inp["cu_q_host"]
+    st = inp["steps"][step]
+    kp, cuk = st["k_positions_host"], st["cu_k_host"]
+    total = 0
+    for b in range(len(cu) - 1):
+        total += int(np.searchsorted(kp[cuk[b]:cuk[b + 1]], qp[cu[b]:cu[b + 1]], side="right").sum())
+    return total
+
+
+def paged_pairs(inp, rank: int) -> int:
+    qp, cu = inp["q_positions_host"], inp["cu_q_host"]
+    rk = inp["ranks"][rank]
+    l2g, cul = rk["local_to_global_host"], rk["cu_local_host"]
+    total = 0
+    for b in range(len(cu) - 1):
+        total += int(np.searchsorted(l2g[cul[b]:cul[b + 1]], qp[cu[b]:cu[b + 1]], side="right").sum())
+    return total
+
+
+def merge_bytes(w, rows: int, n_parts: int, out_bytes: int) -> int:
+    return n_parts * rows * (w.d * 4 + 4) + rows * (w.d * out_bytes + 4)
+
+
+# ------------------------------------------------------------------ GPU timing
+
+
+def bench_workload(name: str, steps: int, warmup: int) -> dict:
+    import torch
+
+    from context_partial_attention_amd import harness
+    from context_partial_attention_amd.workloads import WORKLOADS
+
+    w = WORKLOADS[name]
+    t_build = time.perf_counter()
+    inp = harness.build(w, device="cuda", keep_full=False)
+    run = harness.Runner(inp)
+    torch.cuda.synchronize()
+    log(f"[bench] {name}: inputs built in {time.perf_counter() - t_build:.1f} s")
+    stream = torch.cuda.current_stream()
+    if w.kind == "pass_kv":
+        own = list(range(w.cp))  # every step is this rank's work
+    else:
+        own = [w.rank]  # this rank's paged shard; the other ranks' partials are resident
+        for r in range(w.cp):
+            if r != w.rank:
+                run.partial(r)
+    for _ in range(warmup):
+        for i in own:
+            run.partial(i)
+        run.merge()
+    torch.cuda.synchronize()
+
+    ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
+    part_ev = [[(ev(), ev()) for _ in own] for _ in range(steps)]
+    merge_ev = [(ev(), ev()) for _ in range(steps)]
+    g0, g1 = ev(), ev()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    g0.record(stream)
+    for k in range(steps):
+        for j, i in enumerate(own):
+            part_ev[k][j][0].record(stream)
+            run.partial(i)
+            part_ev[k][j][1].record(stream)
+        merge_ev[k][0].record(stream)
+        run.merge()
+        merge_ev[k][1].record(stream)
+    g1.record(stream)
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t0) * 1e3
+    gpu_ms = g0.elapsed_time(g1)
+    part_ms = [[a.elapsed_time(b) for a, b in row] for row in part_ev]
+    mrg_ms = [a.elapsed_time(b) for a, b in merge_ev]
+
+    rows = inp["q"].shape[0] * w.hq
+    mbytes = merge_bytes(w, rows, w.cp, 2 if run.merged_dtype == torch.bfloat16 else 4)
+    res = {
+        "kind": w.kind,
+        "description": w.description,
+        "steps": steps,
+        "ms_per_step": wall_ms / steps,
+        "gpu_ms_per_step": gpu_ms / steps,
+        "partial_ms": [float(np.mean([r[j] for r in part_ms])) for j in range(len(own))],
+        "merge_ms": float(np.mean(mrg_ms)),
+        "merge_GBps": mbytes / (np.mean(mrg_ms) * 1e-3) / 1e9,
+        "merge_hbm_frac": mbytes / (np.mean(mrg_ms) * 1e-3) / 1e9 / PEAK_HBM_GBS,
+    }
+    if w.kind == "pass_kv":
+        pairs = [pass_kv_pairs(inp, i) for i in own]
+    else:
+        pairs = [paged_pairs(inp, i) for i in own]
+    flops = [4 * w.d * w.hq * p for p in pairs]
+    res["pairs_per_partial"] = pairs
+    res["flops_per_step"] = int(sum(flops))
+    if w.kind in ("pass_kv", "pass_q"):
+        res["TFLOPs"] = sum(flops) / (res["ms_per_step"] * 1e-3) / 1e12
+        res["pct_bf16_peak"] = 100 * res["TFLOPs"] / PEAK_BF16_TFLOPS
+        tot_part_ms = sum(sum(r) for r in part_ms)
+        res["partial_TFLOPs"] = sum(flops) * steps / (tot_part_ms * 1e-3) / 1e12
+        res["partial_pct_bf16_peak"] = 100 * res["partial_TFLOPs"] / PEAK_BF16_TFLOPS
+    else:
+        # decode: K and V of every visible local token, q, O (fp32) and LSE
+        rk = inp["ranks"][w.rank]
+        kv_bytes = 2 * w.hkv * w.d * 2 * pairs[0]  # one query per sequence: pairs == visible tokens
+        nq = inp["q"].shape[0]
+        io_bytes = nq * w.hq * w.d * 2 + nq * w.hq * (w.d * 4 + 4)
+        part_bytes = kv_bytes + io_bytes
+        res["partial_bytes"] = int(part_bytes)
+        res["partial_GBps"] = part_bytes / (res["partial_ms"][0] * 1e-3) / 1e9
+        res["partial_hbm_frac"] = res["partial_GBps"] / PEAK_HBM_GBS
+        res["GBps"] = (part_bytes + mbytes) / (res["ms_per_step"] * 1e-3) / 1e9
+        res["hbm_frac"] = res["GBps"] / PEAK_HBM_GBS
+        del rk
+    if w.kind == "pass_kv":
+        res["seq_lens"] = inp["lens"]
+    del run, inp
+    torch.cuda.empty_cache()
+    return res
+
+
+# ------------------------------------------------------------------ traffic from committed counters
+
+
+def _source_digest() -> str:
+    h = hashlib.sha256()
+    for f in ("attn_mfma.hip", "device_common.h"):
+        with open(os.path.join(ROOT, "context_partial_attention_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def committed_traffic():
+    """HBM bytes per launch of the partial-attention kernel on the headline
+    workload, from the committed rocprofv3 counter summary; None when it is
+    missing or was taken from a different kernel source."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    vals = {}
+    with open(TRAFFIC_FILE) as f:
+        for line in f:
+            if line.startswith("- ") and ":" in line:
+                k, v = line[2:].split(":", 1)
+                vals[k.strip()] = v.strip().strip("`")
+    if vals.get("kernel_source_digest") != _source_digest():
+        return None
+    try:
+        return float(vals["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+# ------------------------------------------------------------------ CPU baseline (oracle)
+
+
+def cpu_baseline(name: str, budget_s: float = 10.0) -> dict:
+    """Times the oracle on the host on a bounded sample of the headline
+    workload: whole sequences (rank 0's shard, all heads, both pass-KV steps
+    and the merge), added one by one until about `budget_s` of CPU work."""
+    import torch
+    from threadpoolctl import threadpool_info
+
+    import oracle
+    from context_partial_attention_amd.workloads import WORKLOADS, draw_sequence, seq_lengths
+
+    w = WORKLOADS[name]
+    lens = seq_lengths(w)
+    done_flops, elapsed, used = 0, 0.0, 0
+    for b, L in enumerate(lens):
+        q, k, v = (t.float().numpy().astype(np.float64) for t in draw_sequence(w, b, L, L, device="cpu"))
+        t0 = time.perf_counter()
+        mine = oracle.zigzag_partition([L], w.cp, w.rank)
+        qp = mine["positions"]
+        parts, kps = [], []
+        for s in range(w.cp):
+            src = oracle.zigzag_partition([L], w.cp, (w.rank - s) % w.cp)
+            kp = src["positions"]
+            kps.append(kp)
+            parts.append(oracle.partial_attn(q[qp], qp, [0, len(qp)], k[kp], v[kp], kp, [0, len(kp)], w.scale))
+        oracle.lse_merge([p[0] for p in parts], [p[1] for p in parts])
+        elapsed += time.perf_counter() - t0
+        pairs = sum(int(np.searchsorted(kp, qp, side="right").sum()) for kp in kps)
+        done_flops += 4 * w.d * w.hq * pairs
+        used += 1
+        if elapsed >= budget_s:
+            break
+    del torch
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    return {
+        "value": done_flops / elapsed / 1e12,
+        "unit": "TFLOP/s",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": f"sequences 0..{used - 1} of {len(lens)} (lengths {lens[:used]}), rank {w.rank}'s zigzag shard, "
+                  f"all {w.hq} heads, {w.cp} pass-KV steps + merge, fp64 NumPy; {elapsed:.1f} s",
+        "seconds": elapsed,
+        "cpu": platform.processor() or platform.machine(),
+    }
+
+
+# ------------------------------------------------------------------ main
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workloads", type=str, default=",".join(DEFAULT_WORKLOADS))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run a plain device-to-device copy of 256 MiB (x4) to scale HBM byte counters")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for --gpus {args.gpus}); "
+              "the whole-job value is the one GPU's throughput at --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import context_partial_attention_amd as cpa
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    cpa.load_library()
+    if args.calibrate_copy:
+        n = 256 << 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(4):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibrate_copy_bytes_per_dispatch": n, "dispatches": 4}), flush=True)
+        return
+    names = [n for n in args.workloads.split(",") if n]
+    if HEADLINE not in names:
+        names = [HEADLINE] + names
+    results = {}
+    for name in names:
+        log(f"[bench] {name}: {args.warmup} warmup + {args.steps} timed steps")
+        results[name] = bench_workload(name, args.steps, args.warmup)
+        log(f"[bench] {name}: {json.dumps({k: v for k, v in results[name].items() if k != 'description'})}")
+    h = results[HEADLINE]
+    # dominant kernel of the headline: the partial-attention launches
+    part_ms = float(np.mean(h["partial_ms"]))
+    flops_per_launch = h["flops_per_step"] / len(h["partial_ms"])
+    achieved = flops_per_launch / (part_ms * 1e-3) / 1e12
+    traffic = committed_traffic()
+    line = {
+        "metric": METRIC,
+        "value": h["TFLOPs"],
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": h["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "pct_bf16_mfma_peak": h["pct_bf16_peak"],
+        "config": {
+            "workload": HEADLINE,
+            "seq_lens": h["seq_lens"],
+            "cp": 2,
+            "rank": 0,
+            "hq": 16,
+            "hkv": 2,
+            "d": 128,
+            "step": "2 pass-KV partial attentions + 2-way LSE merge (bf16 out)",
+        },
+        "roofline": {
+            "kernel": "attn_mfma_kernel<128, contiguous, fp32 out>",
+            "bound": "mfma",
+            "achieved": achieved,
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": achieved / PEAK_BF16_TFLOPS,
+            "traffic": traffic,
+            "avg_launch_ms": part_ms,
+            "flops_per_launch": flops_per_launch,
+        },
+        "workloads": {k: v for k, v in results.items() if k != HEADLINE},
+    }
+    if not args.no_cpu_baseline:
+        log("[bench] cpu baseline (oracle) ...")
+        line["cpu_baseline"] = cpu_baseline(HEADLINE)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

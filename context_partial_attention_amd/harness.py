@@ -120,6 +120,8 @@ def _build_paged(w, lens, draws, device, out, pool_fill):
             "block_table": tab_dev,
             "local_kv_lens": _i32(pl["local_lens"], device),
             "local_lens_host": pl["local_lens"],
+            "local_to_global_host": pl["local_to_global"],
+            "cu_local_host": pl["cu_local"],
         })
     out["ranks"] = ranks
 
