@@ -29,6 +29,7 @@ SOURCES = [
     "lse_merge.hip",
     "attn_f32.hip",
     "attn_mfma.hip",
+    "attn_pp.hip",
     "attn_decode.hip",
 ]
 

@@ -66,7 +66,7 @@ extern "C" cpa_status cpa_partial_attn(const void* q, const int32_t* q_pos, cons
   a.lse = lse;
   hipStream_t s = (hipStream_t)stream;
   if (in_dtype == CPA_F32) return launch_attn_f32(a, s);
-  return launch_attn_mfma(a, /*paged=*/false, s);
+  return attn_pp_supported(a) ? launch_attn_pp(a, /*paged=*/false, s) : launch_attn_mfma(a, /*paged=*/false, s);
 }
 
 extern "C" cpa_status cpa_partial_attn_paged_workspace(int32_t num_seqs, int32_t max_q, int32_t max_blocks,
@@ -140,5 +140,6 @@ extern "C" cpa_status cpa_partial_attn_paged(const void* q, const int32_t* q_pos
   a.workspace = workspace;
   a.workspace_bytes = workspace_bytes;
   hipStream_t s = (hipStream_t)stream;
-  return decode ? launch_attn_decode(a, s) : launch_attn_mfma(a, /*paged=*/true, s);
+  if (decode) return launch_attn_decode(a, s);
+  return attn_pp_supported(a) ? launch_attn_pp(a, /*paged=*/true, s) : launch_attn_mfma(a, /*paged=*/true, s);
 }

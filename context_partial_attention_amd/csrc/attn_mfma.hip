@@ -432,7 +432,7 @@ __global__ __launch_bounds__(kThreads, 3 - RB) void attn_mfma_kernel(Params p) {
       store_tile(vbuf((t + 1) & 1), T::kVStride, vreg);
       if (tid < kBN) kpos_sh[(t + 1) & 1][tid] = kp_reg;
     }
-    __syncthreads();
+    lds_barrier();
   };
 
   // The loop is reached only through the prologue, which waits for every load

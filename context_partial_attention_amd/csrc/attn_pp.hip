@@ -1,0 +1,473 @@
+// Partial causal GQA attention on bf16 inputs: two-group ("ping-pong")
+// workgroup for GQA groups of even size.
+//
+// Computes the same partial attention as attn_mfma.hip (a packed query shard
+// against one KV shard, causal in global positions, returning O and the
+// natural-log LSE; "Add utility functions to enable pass-kv prefill and
+// allgather decode", Purpose) with a schedule built to keep the matrix cores
+// busy while the softmax runs.
+//
+// A workgroup of 8 waves owns 128 query rows of two heads h0, h0+1 of one GQA
+// group (they read the same KV head). Waves 0-3 (group 0) take head h0,
+// waves 4-7 (group 1) head h0+1; each wave owns 32 rows, so every SIMD holds
+// one wave of each group. Work on KV tile t is split into two phases:
+//   A(t): O += V(t-1)^T P(t-1)^T and S(t)^T = K(t) Q^T   (matrix cores)
+//   B(t): mask, online softmax of S(t) -> P(t)           (vector ALUs)
+// Group 1 runs one phase behind group 0 and every phase ends with a
+// workgroup barrier, so on each SIMD one wave issues MFMAs while the other
+// does its softmax. Both groups see the same rows, hence the same masks and
+// tile counts, so neither waits on the other.
+//
+// LDS holds two slots; slot t carries K(t), V(t-1) and the key positions of
+// tile t and is read in phases 2t and 2t+1. Its global loads are issued at
+// the start of phase 2t-2 and written to LDS at the end of phase 2t-1, so
+// every load has two phases to arrive. V is transposed on its way into LDS
+// (d-major, keys permuted to match the S^T accumulator order), so both K and
+// V^T operands are single 16-byte LDS reads, which run at about twice the
+// bandwidth of transposing reads; rows are padded so reads and writes are
+// bank-conflict free.
+#include <climits>
+
+#include "cpa_internal.h"
+#include "device_common.h"
+
+namespace cpa {
+namespace {
+
+constexpr int kBN = 64;        // keys per tile
+constexpr int kRows = 128;     // query rows per workgroup (per head)
+constexpr int kThreads = 512;  // 8 waves
+
+template <int D>
+struct PPTile {
+  static constexpr int kKStride = D + 8;   // 16-byte K reads: 4 banks apart per row
+  // V is stored transposed (d-major, one row per head dim holding the tile's
+  // 64 keys): rows 36 dwords apart make the 16-byte operand reads and the
+  // 4-byte key-pair writes bank-conflict free
+  static constexpr int kVStride = kBN + 8;
+  static constexpr int kKElems = kBN * kKStride;
+  static constexpr int kVElems = D * kVStride;
+  static constexpr int kVUnits = (kBN / 2) * (D / 8);  // (key pair, 8 dims) pieces of a V tile
+  static constexpr int kSlotElems = kKElems + kVElems;
+  static constexpr int kChunksPerRow = D / 8;
+  static constexpr int kChunks = kBN * kChunksPerRow / kThreads;  // 16-byte pieces per thread per matrix
+  static constexpr int kRowsPerPass = kThreads / kChunksPerRow;
+  static_assert(kChunks >= 1 && kChunks * kThreads == kBN * kChunksPerRow, "tile must split evenly");
+  static_assert(kRowsPerPass % 16 == 0 && 16 % (64 / kChunksPerRow) == 0, "wave rows must share a block");
+  static_assert(kVUnits <= kThreads, "one V piece per thread at most");
+};
+
+struct PPParams {
+  const uint16_t* q;
+  const int* q_pos;
+  const int* cu_q;
+  const uint16_t* k;
+  const uint16_t* v;
+  const int* k_pos;
+  const int* cu_k;
+  const int* block_table;
+  int max_blocks;
+  const int* local_kv_lens;
+  int cp, rank, il;
+  int num_seqs, hq, hkv, g, n_groups;
+  float scale_log2;
+  int causal;
+  void* o;
+  float* lse;
+};
+
+// Column (LDS slot) of key `key` in a transposed V tile: within every 16
+// keys the groups of 4 are stored in the order 0,2,1,3 (bits 2 and 3
+// swapped), the order in which a lane's half of the S^T accumulator lists
+// them, so that a lane's 8 P values meet 8 contiguous V values.
+__device__ __forceinline__ int pp_v_slot(int key) { return (key & ~12) | ((key & 4) << 1) | ((key & 8) >> 1); }
+
+__device__ __forceinline__ float pp_max3(float a, float b, float c) { return fmaxf(a, fmaxf(b, c)); }
+
+// Entries of the ascending array a[0..n) that are <= x (whole workgroup).
+__device__ int pp_count_le(const int* __restrict__ a, int n, int x) {
+  int lo = 0, hi = n;
+  while (true) {
+    const int span = hi - lo;
+    if (span <= 0) return lo;
+    const int step = (span + kThreads - 1) / kThreads;
+    const int idx = lo + (int)(threadIdx.x + 1) * step - 1;
+    const int c = __syncthreads_count(idx < hi && a[idx] <= x);
+    const int new_lo = lo + c * step;
+    if (step == 1) return new_lo;
+    hi = min(hi, new_lo + step - 1);
+    lo = new_lo;
+  }
+}
+
+template <int D, bool PAGED, bool OUT_BF16>
+__global__ __launch_bounds__(kThreads, 1) void attn_pp_kernel(PPParams p) {
+  using T = PPTile<D>;
+  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * T::kSlotElems];
+  __shared__ int kpos_sh[2][kBN];
+
+  // ---- (sequence, query tile, KV head) group and head pair; the head pairs
+  // of a group share an XCD, consecutive groups rotate over the 8 XCDs
+  const int pairs = p.g >> 1;
+  const int id = blockIdx.x;
+  const int xcd = id & 7, rest = id >> 3;
+  const int pair = rest % pairs;
+  const int grow = rest / pairs;
+  const int grp = grow * 8 + ((xcd - grow) & 7);
+  if (grp >= p.n_groups) return;
+  const int kvh = grp % p.hkv;
+  const int t2 = grp / p.hkv;
+  const int seq = t2 % p.num_seqs;
+  const int t_desc = t2 / p.num_seqs;
+  const int qa = p.cu_q[seq], qe = p.cu_q[seq + 1];
+  const int n_tiles = (qe - qa + kRows - 1) / kRows;
+  if (t_desc >= n_tiles) return;
+  const int row0 = qa + (n_tiles - 1 - t_desc) * kRows;
+
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int gp = wave >> 2, wq = wave & 3;  // group, 32-row block
+  const int lr = lane & 31, lc = lane >> 5;
+  const int h = kvh * p.g + 2 * pair + gp;
+
+  // ---- rows and positions (both groups see the same rows)
+  const int my_row = row0 + 32 * wq + lr;
+  const bool row_ok = my_row < qe;
+  const int wave_first = row0 + 32 * wq;
+  const bool wave_active = wave_first < qe;
+  const int wave_last = min(wave_first + 31, qe - 1);
+  const int blk_last = min(row0 + kRows - 1, qe - 1);
+  int my_pos, wave_qmin, wave_qmax, blk_qmax;
+  if (p.causal) {
+    my_pos = row_ok ? p.q_pos[my_row] : INT_MIN;
+    wave_qmin = __builtin_amdgcn_readfirstlane(wave_active ? p.q_pos[wave_first] : INT_MIN);
+    wave_qmax = __builtin_amdgcn_readfirstlane(wave_active ? p.q_pos[wave_last] : INT_MIN);
+    blk_qmax = p.q_pos[blk_last];
+  } else {
+    my_pos = row_ok ? INT_MAX - 1 : INT_MIN;
+    wave_qmin = wave_qmax = wave_active ? INT_MAX - 1 : INT_MIN;
+    blk_qmax = INT_MAX - 1;
+  }
+
+  // ---- key range [ka, n_end) some row of the workgroup can see
+  int ka, ke;
+  if constexpr (PAGED) {
+    ka = 0;
+    ke = min(p.local_kv_lens[seq], p.max_blocks * 16);  // never index past the block table
+  } else {
+    ka = p.cu_k[seq];
+    ke = p.cu_k[seq + 1];
+  }
+  int n_end = ke;
+  if (p.causal) {
+    if constexpr (PAGED) n_end = min(ke, rr_count_below(blk_qmax + 1, p.cp, p.rank, p.il));
+    else n_end = ka + pp_count_le(p.k_pos + ka, ke - ka, blk_qmax);
+  }
+  const int n = n_end > ka ? (n_end - ka + kBN - 1) / kBN : 0;  // tiles
+
+  // ---- Q^T fragments
+  bf16x8 qf[D / 16];
+  {
+    const int qrow = row_ok ? my_row : qa;
+    const uint16_t* src = p.q + ((int64_t)qrow * p.hq + h) * D + 8 * lc;
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk) qf[kk] = *(const bf16x8*)(src + 16 * kk);
+  }
+
+  // ---- slot staging: piece i of a matrix covers row r_first + i*kRowsPerPass
+  const int c8 = tid % T::kChunksPerRow;
+  const int r_first = tid / T::kChunksPerRow;
+  const int64_t row_stride = (int64_t)p.hkv * D;
+  uint32_t off[T::kChunks];
+#pragma unroll
+  for (int i = 0; i < T::kChunks; ++i) {
+    const int r = r_first + i * T::kRowsPerPass;
+    if constexpr (PAGED) off[i] = (uint32_t)((r & 15) * D + c8 * 8);
+    else off[i] = (uint32_t)(r * row_stride + c8 * 8);
+  }
+  auto load_tile = [&](const uint16_t* __restrict__ src, int t, u32x4* regs) {
+    const int j0 = ka + t * kBN;
+    const bool last = j0 + kBN > n_end;
+    if constexpr (PAGED) {
+      const int64_t slab = (int64_t)p.hkv * 16 * D;
+      const int* tab = p.block_table + (int64_t)seq * p.max_blocks;
+#pragma unroll
+      for (int i = 0; i < T::kChunks; ++i) {
+        const int r = r_first + i * T::kRowsPerPass;
+        if (!last) {
+          const int blk = tab[__builtin_amdgcn_readfirstlane((j0 + r) >> 4)];
+          regs[i] = *(const u32x4*)(src + (int64_t)blk * slab + (int64_t)kvh * 16 * D + off[i]);
+        } else {
+          const int j = min(j0 + r, n_end - 1);
+          const int blk = tab[j >> 4];
+          regs[i] = *(const u32x4*)(src + (int64_t)blk * slab + ((int64_t)kvh * 16 + (j & 15)) * D + c8 * 8);
+        }
+      }
+    } else {
+      const uint16_t* b = src + ((int64_t)j0 * p.hkv + kvh) * D;
+#pragma unroll
+      for (int i = 0; i < T::kChunks; ++i) {
+        uint32_t o = off[i];
+        if (last) o = (uint32_t)(min(r_first + i * T::kRowsPerPass, n_end - 1 - j0) * row_stride + c8 * 8);
+        regs[i] = *(const u32x4*)(b + o);
+      }
+    }
+  };
+  // V piece of thread tid < kVUnits: keys 2 kp, 2 kp + 1 of the tile, dims 8 dc .. 8 dc + 7
+  const int v_kp = tid % (kBN / 2), v_dc = tid / (kBN / 2);
+  auto load_v = [&](int t, u32x4* regs) {
+    if (tid >= T::kVUnits) return;
+    const int j0 = ka + t * kBN;
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+      const int j = min(j0 + 2 * v_kp + r, n_end - 1);
+      if constexpr (PAGED) {
+        const int blk = p.block_table[(int64_t)seq * p.max_blocks + (j >> 4)];
+        regs[r] = *(const u32x4*)(p.v + ((int64_t)blk * p.hkv + kvh) * 16 * D + (j & 15) * D + v_dc * 8);
+      } else {
+        regs[r] = *(const u32x4*)(p.v + ((int64_t)j * p.hkv + kvh) * D + v_dc * 8);
+      }
+    }
+  };
+  auto key_pos = [&](int t) -> int {  // position of key tid of tile t (tid < 64), INT_MAX past the end
+    const int j = ka + t * kBN + tid;
+    if (j >= n_end) return INT_MAX;
+    if constexpr (PAGED) return rr_global_pos(j, p.cp, p.rank, p.il);
+    else return p.causal ? p.k_pos[j] : 0;
+  };
+  auto kslot = [&](int s) { return smem + s * T::kSlotElems; };
+  auto vslot = [&](int s) { return smem + s * T::kSlotElems + T::kKElems; };
+  auto store_tile = [&](uint16_t* dst, int stride, const u32x4* regs) {
+#pragma unroll
+    for (int i = 0; i < T::kChunks; ++i)
+      *(u32x4*)(dst + (r_first + i * T::kRowsPerPass) * stride + c8 * 8) = regs[i];
+  };
+
+  u32x4 kreg[T::kChunks], vreg[2];
+  int kp_reg = INT_MAX;
+  // slot t = {K(t), V(t-1), positions of tile t}
+  auto load_slot = [&](int t) {
+    if (t < n) {
+      load_tile(p.k, t, kreg);
+      if (tid < kBN) kp_reg = key_pos(t);
+    }
+    if (t >= 1) load_v(t - 1, vreg);
+  };
+  auto store_slot = [&](int t) {
+    const int s = t & 1;
+    if (t < n) {
+      store_tile(kslot(s), T::kKStride, kreg);
+      if (tid < kBN) kpos_sh[s][tid] = kp_reg;
+    }
+    if (t >= 1 && tid < T::kVUnits) {
+      // transpose the key pair into 8 dim rows: one 4-byte (key, key+1) pair per row
+      uint16_t* vt = vslot(s) + (8 * v_dc) * T::kVStride + pp_v_slot(2 * v_kp);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t w0 = vreg[0][e], w1 = vreg[1][e];
+        *(uint32_t*)(vt + (2 * e) * T::kVStride) = (w0 & 0xffffu) | (w1 << 16);
+        *(uint32_t*)(vt + (2 * e + 1) * T::kVStride) = (w0 >> 16) | (w1 & 0xffff0000u);
+      }
+    }
+  };
+
+  // ---- per-wave state
+  f32x16 oacc[D / 32];
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db) oacc[db] = f32x16{};
+  float m_run = kNegInf, l_run = 0.f;
+  const float sl2 = p.scale_log2;
+  constexpr float kTau = 8.f;  // lazy-rescale threshold (log2 units)
+  f32x16 s0 = {}, s1 = {};  // S(t) after phase A, P(t) in fp32 after phase B
+  bool p_valid = false;     // s0/s1 hold P of the previous tile for this wave
+
+  const int k_lane = lr * T::kKStride + 8 * lc;
+  const int v_lane = lr * T::kVStride + 8 * lc;  // V^T rows (dims) lr (+32 db), slots 16 kst + 8 lc
+
+  // A(t): O += V(t-1)^T P(t-1)^T, then S(t)^T = K(t) Q^T. The bf16 packing of
+  // P(t-1) and its row sum run here, under the matrix work, to keep the
+  // softmax phase short.
+  auto phase_a = [&](int t) {
+    const int s = t & 1;
+    if (t >= 1 && p_valid) {
+      bf16x8 pb[4];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        pb[0][e] = (__bf16)s0[e];
+        pb[1][e] = (__bf16)s0[8 + e];
+        pb[2][e] = (__bf16)s1[e];
+        pb[3][e] = (__bf16)s1[8 + e];
+      }
+      float ps = 0.f;
+#pragma unroll
+      for (int v = 0; v < 16; ++v) ps += s0[v] + s1[v];
+      l_run += ps;
+      const uint16_t* vs = vslot(s) + v_lane;
+      // operand i = (k-step i / (D/32), d-block i % (D/32)); consecutive MFMAs
+      // accumulate into different d-blocks, and the transposing reads run
+      // kVPre operands ahead
+      constexpr int kOps = 4 * (D / 32), kVPre = 4;
+      auto vop = [&](int i) {
+        return *(const bf16x8*)(vs + 32 * (i % (D / 32)) * T::kVStride + 16 * (i / (D / 32)));
+      };
+      bf16x8 va[kVPre];
+#pragma unroll
+      for (int i = 0; i < kVPre; ++i) va[i] = vop(i);
+#pragma unroll
+      for (int i = 0; i < kOps; ++i) {
+        __builtin_amdgcn_sched_barrier(0);
+        const int db = i % (D / 32), kst = i / (D / 32);
+        oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[i % kVPre], pb[kst], oacc[db], 0, 0, 0);
+        if (i + kVPre < kOps) va[i % kVPre] = vop(i + kVPre);
+      }
+    }
+    if (t < n && __builtin_amdgcn_readfirstlane(kpos_sh[s][0]) <= wave_qmax) {
+      const uint16_t* ks = kslot(s) + k_lane;
+      s0 = f32x16{};
+      s1 = f32x16{};
+      // K operands read kPre steps ahead of their MFMAs (a ring of registers),
+      // so LDS latency overlaps the matrix work
+      constexpr int kPre = 3;
+      bf16x8 ra[kPre], rb[kPre];
+#pragma unroll
+      for (int kk = 0; kk < kPre; ++kk) {
+        ra[kk] = *(const bf16x8*)(ks + 16 * kk);
+        rb[kk] = *(const bf16x8*)(ks + 32 * T::kKStride + 16 * kk);
+      }
+#pragma unroll
+      for (int kk = 0; kk < D / 16; ++kk) {
+        __builtin_amdgcn_sched_barrier(0);
+        s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ra[kk % kPre], qf[kk], s0, 0, 0, 0);
+        s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rb[kk % kPre], qf[kk], s1, 0, 0, 0);
+        if (kk + kPre < D / 16) {
+          ra[kk % kPre] = *(const bf16x8*)(ks + 16 * (kk + kPre));
+          rb[kk % kPre] = *(const bf16x8*)(ks + 32 * T::kKStride + 16 * (kk + kPre));
+        }
+      }
+    }
+  };
+
+  // B(t): mask and online softmax of S(t) -> P(t) (fp32, in place)
+  auto phase_b = [&](int t) {
+    const int* kp = kpos_sh[t & 1];
+    p_valid = __builtin_amdgcn_readfirstlane(kp[0]) <= wave_qmax;
+    if (!p_valid) return;
+    // accumulator element v of this lane holds key 8*(v/4) + 4*lc + v%4 (+32 for s1)
+    if (__builtin_amdgcn_readfirstlane(kp[kBN - 1]) > wave_qmin) {
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int key = 8 * (v >> 2) + 4 * lc + (v & 3);
+        if (kp[key] > my_pos) s0[v] = kNegInf;
+        if (kp[32 + key] > my_pos) s1[v] = kNegInf;
+      }
+    }
+    float mx = fmaxf(s0[0], s1[0]);
+#pragma unroll
+    for (int v = 1; v < 16; ++v) mx = pp_max3(mx, s0[v], s1[v]);
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * sl2;
+    if (__ballot(mx > m_run + kTau) != 0) {
+      const float m_new = fmaxf(m_run, mx);
+      const float alpha = (m_new == kNegInf) ? 1.f : hw_exp2(m_run - m_new);
+      l_run *= alpha;
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db) oacc[db] *= alpha;
+      m_run = m_new;
+    }
+    const float base = (m_run == kNegInf) ? 0.f : m_run;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      s0[v] = hw_exp2(fmaf(s0[v], sl2, -base));
+      s1[v] = hw_exp2(fmaf(s1[v], sl2, -base));
+    }
+  };
+
+  if (n > 0) {
+    load_slot(0);
+    store_slot(0);
+    __syncthreads();
+    // phases 0 .. 2n+1; group 0 runs A(t) in phase 2t and B(t) in 2t+1,
+    // group 1 one phase later; slot t+1 is loaded during phases 2t, 2t+1
+    for (int ph = 0; ph <= 2 * n + 1; ++ph) {
+      const int t_ld = ph >> 1;
+      if (!(ph & 1) && t_ld + 1 <= n) load_slot(t_ld + 1);
+      const int q = ph - gp;  // this group's own phase index
+      if (q >= 0 && q <= 2 * n) {
+        if (!(q & 1)) phase_a(q >> 1);
+        else phase_b(q >> 1);
+      }
+      if ((ph & 1) && t_ld + 1 <= n) store_slot(t_ld + 1);
+      lds_barrier();
+    }
+  }
+
+  // ---- epilogue
+  const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
+  if (!row_ok) return;
+  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+  const int64_t obase = ((int64_t)my_row * p.hq + h) * D;
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db) {
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      const int d0 = 32 * db + 8 * q4 + 4 * lc;
+      const f32x4 val = {oacc[db][4 * q4] * inv, oacc[db][4 * q4 + 1] * inv, oacc[db][4 * q4 + 2] * inv,
+                         oacc[db][4 * q4 + 3] * inv};
+      if constexpr (OUT_BF16) {
+        const u32x2 w = {pack_bf16x2(val[0], val[1]), pack_bf16x2(val[2], val[3])};
+        *(u32x2*)((uint16_t*)p.o + obase + d0) = w;
+      } else {
+        *(f32x4*)((float*)p.o + obase + d0) = val;
+      }
+    }
+  }
+  if (lc == 0) p.lse[(int64_t)my_row * p.hq + h] = l_tot > 0.f ? (m_run + hw_log2(l_tot)) * kLn2 : kNegInf;
+}
+
+template <int D, bool PAGED, bool OUT_BF16>
+void pp_launch(const PPParams& p, uint32_t blocks, hipStream_t st) {
+  hipLaunchKernelGGL((attn_pp_kernel<D, PAGED, OUT_BF16>), dim3(blocks), dim3(kThreads), 0, st, p);
+}
+
+}  // namespace
+
+bool attn_pp_supported(const AttnArgs& a) { return (a.hq / a.hkv) % 2 == 0; }
+
+cpa_status launch_attn_pp(const AttnArgs& a, bool paged, hipStream_t st) {
+  PPParams p{};
+  p.q = (const uint16_t*)a.q;
+  p.q_pos = a.q_pos;
+  p.cu_q = a.cu_q;
+  p.k = (const uint16_t*)a.k;
+  p.v = (const uint16_t*)a.v;
+  p.k_pos = a.k_pos;
+  p.cu_k = a.cu_k;
+  p.block_table = a.block_table;
+  p.max_blocks = a.max_blocks;
+  p.local_kv_lens = a.local_kv_lens;
+  p.cp = a.cp;
+  p.rank = a.rank;
+  p.il = a.interleave;
+  p.num_seqs = a.num_seqs;
+  p.hq = a.hq;
+  p.hkv = a.hkv;
+  p.g = a.hq / a.hkv;
+  p.scale_log2 = a.scale * kLog2e;
+  p.causal = a.causal;
+  p.o = a.o;
+  p.lse = a.lse;
+  const int64_t n_groups = cdiv(a.max_q, kRows) * a.num_seqs * a.hkv;
+  const int64_t blocks = cdiv(n_groups, 8) * 8 * (p.g / 2);
+  if (blocks > INT32_MAX) return fail(CPA_ERR_INVALID_ARG, "partial attention: problem too large for one launch");
+  p.n_groups = (int)n_groups;
+  if (blocks == 0) return CPA_OK;
+  const uint32_t nb = (uint32_t)blocks;
+  if (a.d == 64) {
+    if (paged) a.o_bf16 ? pp_launch<64, true, true>(p, nb, st) : pp_launch<64, true, false>(p, nb, st);
+    else a.o_bf16 ? pp_launch<64, false, true>(p, nb, st) : pp_launch<64, false, false>(p, nb, st);
+  } else {
+    if (paged) a.o_bf16 ? pp_launch<128, true, true>(p, nb, st) : pp_launch<128, true, false>(p, nb, st);
+    else a.o_bf16 ? pp_launch<128, false, true>(p, nb, st) : pp_launch<128, false, false>(p, nb, st);
+  }
+  return check_launch(paged ? "cpa_partial_attn_paged (prefill)" : "cpa_partial_attn (bf16)");
+}
+
+}  // namespace cpa

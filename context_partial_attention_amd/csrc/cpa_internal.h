@@ -61,6 +61,9 @@ struct AttnArgs {
 
 cpa_status launch_attn_f32(const AttnArgs& a, hipStream_t st);
 cpa_status launch_attn_mfma(const AttnArgs& a, bool paged, hipStream_t st);
+// Two-group workgroup for GQA groups of even size (hq / hkv even).
+bool attn_pp_supported(const AttnArgs& a);
+cpa_status launch_attn_pp(const AttnArgs& a, bool paged, hipStream_t st);
 size_t decode_workspace_bytes(int32_t num_seqs, int32_t max_blocks, int32_t block_size, int32_t hq, int32_t d);
 cpa_status launch_attn_decode(const AttnArgs& a, hipStream_t st);
 

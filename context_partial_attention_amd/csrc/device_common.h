@@ -35,6 +35,19 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
   return __builtin_bit_cast(uint32_t, r);
 }
 
+// Workgroup barrier for LDS hand-offs only. __syncthreads() also waits for
+// every outstanding global load of the wave (its release fence is a full
+// s_waitcnt), which would expose the latency of tiles prefetched for later
+// steps; here only LDS operations (lgkmcnt) must complete before s_barrier.
+// The signal fences keep the compiler from moving memory accesses across it;
+// a load's own consumer still gets its vmcnt wait from the compiler.
+__device__ __forceinline__ void lds_barrier() {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(0xc07f);  // vmcnt and expcnt unconstrained, lgkmcnt(0)
+  __builtin_amdgcn_s_barrier();
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
 __device__ __forceinline__ float wave_max(float x) {
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) x = fmaxf(x, __shfl_xor(x, off, 64));
