@@ -57,6 +57,13 @@ def load_library():
     lib.cpa_partial_attn.restype = _i32
     lib.cpa_partial_attn.argtypes = [_p, _p, _p, _p, _p, _p, _p, _i32, _i32, _i32, _i32, _i32, _i32, _f32, _i32,
                                      _p, _i32, _p, _p]
+    lib.cpa_partial_attn_multi_workspace.restype = _i32
+    lib.cpa_partial_attn_multi_workspace.argtypes = [_i32, _i32, _i32, ctypes.POINTER(ctypes.c_size_t)]
+    lib.cpa_partial_attn_multi.restype = _i32
+    lib.cpa_partial_attn_multi.argtypes = [_i32, _p, _p, _p, ctypes.POINTER(_p), ctypes.POINTER(_p),
+                                           ctypes.POINTER(_p), ctypes.POINTER(_p), _i32, _i32, _i32, _i32, _i32,
+                                           _i32, _f32, _i32, ctypes.POINTER(_p), _i32, ctypes.POINTER(_p), _p,
+                                           ctypes.c_size_t, _p]
     lib.cpa_partial_attn_paged_workspace.restype = _i32
     lib.cpa_partial_attn_paged_workspace.argtypes = [_i32, _i32, _i32, _i32, _i32, _i32,
                                                      ctypes.POINTER(ctypes.c_size_t)]
@@ -174,6 +181,41 @@ def partial_attn(q, q_pos, cu_q, k, v, k_pos, cu_k, max_q: int, scale: float, ca
         MASK_CAUSAL if causal else MASK_NONE, _dev(out, "out"), _dtype_code(out), _dev(lse, "lse"),
         _stream(stream)))
     return out, lse
+
+
+def partial_attn_multi_workspace(n_shards: int, num_seqs: int, max_q: int) -> int:
+    """Bytes of the launch-order workspace of partial_attn_multi (0: none used)."""
+    n = ctypes.c_size_t(0)
+    _check("cpa_partial_attn_multi_workspace",
+           load_library().cpa_partial_attn_multi_workspace(n_shards, num_seqs, int(max_q), ctypes.byref(n)))
+    return n.value
+
+
+def partial_attn_multi(q, q_pos, cu_q, ks, vs, k_poss, cu_ks, max_q: int, scale: float, causal: bool = True,
+                       outs=None, lses=None, out_dtype=None, workspace=None, stream=None):
+    """Several pass-KV steps at once: q against each resident shard (ks[i], vs[i], k_poss[i], cu_ks[i]).
+    `workspace` (a uint8 GPU tensor of partial_attn_multi_workspace() bytes, or None) enables the
+    heaviest-tile-first launch order. Returns the lists (outs, lses), one partial per shard."""
+    torch = _torch()
+    tq, hq, d = q.shape
+    n = len(ks)
+    hkv = ks[0].shape[1]
+    out_dtype = out_dtype or torch.float32
+    if outs is None:
+        outs = [torch.empty((tq, hq, d), dtype=out_dtype, device=q.device) for _ in range(n)]
+    if lses is None:
+        lses = [torch.empty((tq, hq), dtype=torch.float32, device=q.device) for _ in range(n)]
+    if not (len(vs) == len(k_poss) == len(cu_ks) == len(outs) == len(lses) == n):
+        raise ValueError("every per-shard list needs one entry per shard")
+    arr = lambda ts, name: (_p * n)(*[_dev(t, name) for t in ts])  # noqa: E731
+    num_seqs = cu_q.numel() - 1
+    _check("cpa_partial_attn_multi", load_library().cpa_partial_attn_multi(
+        n, _dev(q, "q"), _dev(q_pos, "q_pos"), _dev(cu_q, "cu_q"), arr(ks, "k"), arr(vs, "v"), arr(k_poss, "k_pos"),
+        arr(cu_ks, "cu_k"), num_seqs, int(max_q), hq, hkv, d, _dtype_code(q), float(scale),
+        MASK_CAUSAL if causal else MASK_NONE, arr(outs, "out"), _dtype_code(outs[0]), arr(lses, "lse"),
+        _dev(workspace, "workspace"), 0 if workspace is None else workspace.numel() * workspace.element_size(),
+        _stream(stream)))
+    return outs, lses
 
 
 def partial_attn_paged_workspace(num_seqs: int, max_q: int, max_blocks: int, block_size: int, hq: int,

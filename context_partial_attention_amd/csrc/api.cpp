@@ -66,7 +66,73 @@ extern "C" cpa_status cpa_partial_attn(const void* q, const int32_t* q_pos, cons
   a.lse = lse;
   hipStream_t s = (hipStream_t)stream;
   if (in_dtype == CPA_F32) return launch_attn_f32(a, s);
-  return attn_pp_supported(a) ? launch_attn_pp(a, /*paged=*/false, s) : launch_attn_mfma(a, /*paged=*/false, s);
+  return attn_pp_supported(a) ? launch_attn_pp(&a, 1, /*paged=*/false, s) : launch_attn_mfma(a, /*paged=*/false, s);
+}
+
+extern "C" cpa_status cpa_partial_attn_multi_workspace(int32_t n_shards, int32_t num_seqs, int32_t max_q,
+                                                       size_t* bytes) {
+  if (!bytes) return fail(CPA_ERR_INVALID_ARG, "cpa_partial_attn_multi_workspace: bytes is NULL");
+  if (n_shards < 1 || n_shards > kMaxShards || num_seqs < 0 || max_q < 0)
+    return fail(CPA_ERR_INVALID_ARG, "cpa_partial_attn_multi_workspace: bad sizes");
+  *bytes = attn_pp_order_bytes(n_shards, num_seqs, max_q);
+  return CPA_OK;
+}
+
+extern "C" cpa_status cpa_partial_attn_multi(int32_t n_shards, const void* q, const int32_t* q_pos,
+                                             const int32_t* cu_q, const void* const* k, const void* const* v,
+                                             const int32_t* const* k_pos, const int32_t* const* cu_k,
+                                             int32_t num_seqs, int32_t max_q, int32_t hq, int32_t hkv, int32_t d,
+                                             cpa_dtype in_dtype, float scale, cpa_mask mask, void* const* o,
+                                             cpa_dtype o_dtype, float* const* lse, void* workspace,
+                                             size_t workspace_bytes, void* stream) {
+  const char* fn = "cpa_partial_attn_multi";
+  if (n_shards < 1 || n_shards > kMaxShards)
+    return fail(CPA_ERR_INVALID_ARG, "%s: n_shards %d not in [1, %d]", fn, n_shards, kMaxShards);
+  if (!k || !v || !cu_k || !o || !lse || (mask == CPA_MASK_CAUSAL && !k_pos))
+    return fail(CPA_ERR_INVALID_ARG, "%s: NULL pointer array", fn);
+  if (in_dtype != CPA_BF16 && in_dtype != CPA_F32) return fail(CPA_ERR_INVALID_ARG, "%s: bad in_dtype", fn);
+  if (o_dtype != CPA_BF16 && o_dtype != CPA_F32) return fail(CPA_ERR_INVALID_ARG, "%s: bad o_dtype", fn);
+  if (in_dtype == CPA_F32 && o_dtype != CPA_F32)
+    return fail(CPA_ERR_UNSUPPORTED, "%s: fp32 inputs need an fp32 output", fn);
+  AttnArgs args[kMaxShards];
+  for (int i = 0; i < n_shards; ++i) {
+    const int32_t* kp = (mask == CPA_MASK_CAUSAL) ? k_pos[i] : nullptr;
+    cpa_status st = check_common(fn, q, q_pos, cu_q, k[i], v[i], num_seqs, max_q, hq, hkv, d, scale, mask, o[i], lse[i]);
+    if (st != CPA_OK) return st;
+    if (num_seqs > 0 && max_q > 0) {
+      if (!cu_k[i]) return fail(CPA_ERR_INVALID_ARG, "%s: cu_k[%d] is NULL", fn, i);
+      if (mask == CPA_MASK_CAUSAL && !kp) return fail(CPA_ERR_INVALID_ARG, "%s: k_pos[%d] is NULL", fn, i);
+    }
+    AttnArgs& a = args[i];
+    a.q = q;
+    a.q_pos = q_pos;
+    a.cu_q = cu_q;
+    a.k = k[i];
+    a.v = v[i];
+    a.k_pos = kp;
+    a.cu_k = cu_k[i];
+    a.num_seqs = num_seqs;
+    a.max_q = max_q;
+    a.hq = hq;
+    a.hkv = hkv;
+    a.d = d;
+    a.scale = scale;
+    a.causal = mask == CPA_MASK_CAUSAL;
+    a.o = o[i];
+    a.o_bf16 = o_dtype == CPA_BF16;
+    a.lse = lse[i];
+  }
+  cpa_status st = check_device();
+  if (st != CPA_OK) return st;
+  if (num_seqs == 0 || max_q == 0) return CPA_OK;
+  hipStream_t s = (hipStream_t)stream;
+  if (in_dtype == CPA_BF16 && attn_pp_supported(args[0]))
+    return launch_attn_pp(args, n_shards, /*paged=*/false, s, workspace, workspace_bytes);
+  for (int i = 0; i < n_shards; ++i) {
+    st = (in_dtype == CPA_F32) ? launch_attn_f32(args[i], s) : launch_attn_mfma(args[i], /*paged=*/false, s);
+    if (st != CPA_OK) return st;
+  }
+  return CPA_OK;
 }
 
 extern "C" cpa_status cpa_partial_attn_paged_workspace(int32_t num_seqs, int32_t max_q, int32_t max_blocks,
@@ -141,5 +207,5 @@ extern "C" cpa_status cpa_partial_attn_paged(const void* q, const int32_t* q_pos
   a.workspace_bytes = workspace_bytes;
   hipStream_t s = (hipStream_t)stream;
   if (decode) return launch_attn_decode(a, s);
-  return attn_pp_supported(a) ? launch_attn_pp(a, /*paged=*/true, s) : launch_attn_mfma(a, /*paged=*/true, s);
+  return attn_pp_supported(a) ? launch_attn_pp(&a, 1, /*paged=*/true, s) : launch_attn_mfma(a, /*paged=*/true, s);
 }

@@ -61,10 +61,14 @@ struct PPParams {
   const uint16_t* q;
   const int* q_pos;
   const int* cu_q;
-  const uint16_t* k;
-  const uint16_t* v;
-  const int* k_pos;
-  const int* cu_k;
+  // one entry per KV shard of a batched launch (contiguous shards only)
+  const uint16_t* k[kMaxShards];
+  const uint16_t* v[kMaxShards];
+  const int* k_pos[kMaxShards];
+  const int* cu_k[kMaxShards];
+  void* o[kMaxShards];
+  float* lse[kMaxShards];
+  int n_shards;
   const int* block_table;
   int max_blocks;
   const int* local_kv_lens;
@@ -72,8 +76,9 @@ struct PPParams {
   int num_seqs, hq, hkv, g, n_groups;
   float scale_log2;
   int causal;
-  void* o;
-  float* lse;
+  // Optional launch order (contiguous shards): order[i] is the tile unit
+  // (group / hkv) the i-th unit slot runs; NULL runs units in index order.
+  const int* order;
 };
 
 // Column (LDS slot) of key `key` in a transposed V tile: within every 16
@@ -113,12 +118,22 @@ __global__ __launch_bounds__(kThreads, 1) void attn_pp_kernel(PPParams p) {
   const int xcd = id & 7, rest = id >> 3;
   const int pair = rest % pairs;
   const int grow = rest / pairs;
-  const int grp = grow * 8 + ((xcd - grow) & 7);
+  int grp = grow * 8 + ((xcd - grow) & 7);
   if (grp >= p.n_groups) return;
+  if constexpr (!PAGED) {
+    if (p.order) grp = p.order[grp / p.hkv] * p.hkv + grp % p.hkv;
+  }
+  // group = ((tile_desc * num_seqs + seq) * n_shards + shard) * hkv + kvh:
+  // the heaviest query tiles of every sequence and shard come first
   const int kvh = grp % p.hkv;
   const int t2 = grp / p.hkv;
-  const int seq = t2 % p.num_seqs;
-  const int t_desc = t2 / p.num_seqs;
+  const int shard = t2 % p.n_shards;
+  const int t3 = t2 / p.n_shards;
+  const int seq = t3 % p.num_seqs;
+  const int t_desc = t3 / p.num_seqs;
+  const uint16_t* __restrict__ kmat = p.k[shard];
+  const uint16_t* __restrict__ vmat = p.v[shard];
+  const int* __restrict__ kposv = p.k_pos[shard];
   const int qa = p.cu_q[seq], qe = p.cu_q[seq + 1];
   const int n_tiles = (qe - qa + kRows - 1) / kRows;
   if (t_desc >= n_tiles) return;
@@ -154,13 +169,13 @@ __global__ __launch_bounds__(kThreads, 1) void attn_pp_kernel(PPParams p) {
     ka = 0;
     ke = min(p.local_kv_lens[seq], p.max_blocks * 16);  // never index past the block table
   } else {
-    ka = p.cu_k[seq];
-    ke = p.cu_k[seq + 1];
+    ka = p.cu_k[shard][seq];
+    ke = p.cu_k[shard][seq + 1];
   }
   int n_end = ke;
   if (p.causal) {
     if constexpr (PAGED) n_end = min(ke, rr_count_below(blk_qmax + 1, p.cp, p.rank, p.il));
-    else n_end = ka + pp_count_le(p.k_pos + ka, ke - ka, blk_qmax);
+    else n_end = ka + pp_count_le(kposv + ka, ke - ka, blk_qmax);
   }
   const int n = n_end > ka ? (n_end - ka + kBN - 1) / kBN : 0;  // tiles
 
@@ -222,9 +237,9 @@ __global__ __launch_bounds__(kThreads, 1) void attn_pp_kernel(PPParams p) {
       const int j = min(j0 + 2 * v_kp + r, n_end - 1);
       if constexpr (PAGED) {
         const int blk = p.block_table[(int64_t)seq * p.max_blocks + (j >> 4)];
-        regs[r] = *(const u32x4*)(p.v + ((int64_t)blk * p.hkv + kvh) * 16 * D + (j & 15) * D + v_dc * 8);
+        regs[r] = *(const u32x4*)(vmat + ((int64_t)blk * p.hkv + kvh) * 16 * D + (j & 15) * D + v_dc * 8);
       } else {
-        regs[r] = *(const u32x4*)(p.v + ((int64_t)j * p.hkv + kvh) * D + v_dc * 8);
+        regs[r] = *(const u32x4*)(vmat + ((int64_t)j * p.hkv + kvh) * D + v_dc * 8);
       }
     }
   };
@@ -232,7 +247,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_pp_kernel(PPParams p) {
     const int j = ka + t * kBN + tid;
     if (j >= n_end) return INT_MAX;
     if constexpr (PAGED) return rr_global_pos(j, p.cp, p.rank, p.il);
-    else return p.causal ? p.k_pos[j] : 0;
+    else return p.causal ? kposv[j] : 0;
   };
   auto kslot = [&](int s) { return smem + s * T::kSlotElems; };
   auto vslot = [&](int s) { return smem + s * T::kSlotElems + T::kKElems; };
@@ -247,7 +262,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_pp_kernel(PPParams p) {
   // slot t = {K(t), V(t-1), positions of tile t}
   auto load_slot = [&](int t) {
     if (t < n) {
-      load_tile(p.k, t, kreg);
+      load_tile(kmat, t, kreg);
       if (tid < kBN) kp_reg = key_pos(t);
     }
     if (t >= 1) load_v(t - 1, vreg);
@@ -413,13 +428,93 @@ __global__ __launch_bounds__(kThreads, 1) void attn_pp_kernel(PPParams p) {
                          oacc[db][4 * q4 + 3] * inv};
       if constexpr (OUT_BF16) {
         const u32x2 w = {pack_bf16x2(val[0], val[1]), pack_bf16x2(val[2], val[3])};
-        *(u32x2*)((uint16_t*)p.o + obase + d0) = w;
+        *(u32x2*)((uint16_t*)p.o[shard] + obase + d0) = w;
       } else {
-        *(f32x4*)((float*)p.o + obase + d0) = val;
+        *(f32x4*)((float*)p.o[shard] + obase + d0) = val;
       }
     }
   }
-  if (lc == 0) p.lse[(int64_t)my_row * p.hq + h] = l_tot > 0.f ? (m_run + hw_log2(l_tot)) * kLn2 : kNegInf;
+  if (lc == 0) p.lse[shard][(int64_t)my_row * p.hq + h] = l_tot > 0.f ? (m_run + hw_log2(l_tot)) * kLn2 : kNegInf;
+}
+
+// ---- launch order, heaviest tile units first (contiguous shards)
+//
+// A tile unit is (query tile, sequence, shard); its work is the number of
+// 64-key tiles some row of it can see. With causal masks over zigzag shards
+// that work differs by an order of magnitude between units, and running the
+// heaviest first keeps the tail of the launch short. One workgroup counts
+// every unit's key tiles (a binary search over the first positions of the
+// shard's key tiles) and counting-sorts the units by it, descending. Units
+// of equal work keep no particular order; the results do not depend on it.
+constexpr int kSchedThreads = 1024;
+constexpr int kSchedBuckets = 4096;
+constexpr int kSchedMaxUnits = 8192;
+
+__global__ __launch_bounds__(kSchedThreads) void pp_schedule_kernel(PPParams p, int n_units, int* order) {
+  __shared__ int bucket[kSchedBuckets];
+  __shared__ uint16_t key_sh[kSchedMaxUnits];
+  __shared__ int wave_tot[kSchedThreads / 64];
+  const int tid = threadIdx.x;
+  for (int b = tid; b < kSchedBuckets; b += kSchedThreads) bucket[b] = 0;
+  __syncthreads();
+  for (int u = tid; u < n_units; u += kSchedThreads) {
+    const int shard = u % p.n_shards;
+    const int t3 = u / p.n_shards;
+    const int seq = t3 % p.num_seqs;
+    const int t_desc = t3 / p.num_seqs;
+    const int qa = p.cu_q[seq], qe = p.cu_q[seq + 1];
+    const int n_tiles = (qe - qa + kRows - 1) / kRows;
+    int work = 0;
+    if (t_desc < n_tiles) {
+      const int ka = p.cu_k[shard][seq], ke = p.cu_k[shard][seq + 1];
+      const int nk = (ke - ka + kBN - 1) / kBN;
+      if (!p.causal) {
+        work = nk;
+      } else {
+        const int row0 = qa + (n_tiles - 1 - t_desc) * kRows;
+        const int qmax = p.q_pos[min(row0 + kRows - 1, qe - 1)];
+        const int* kp = p.k_pos[shard] + ka;
+        int lo = 0, hi = nk;  // key tiles whose first key is visible: [0, lo)
+        while (lo < hi) {
+          const int mid = (lo + hi) >> 1;
+          if (kp[mid * kBN] <= qmax) lo = mid + 1;
+          else hi = mid;
+        }
+        work = lo;
+      }
+    }
+    const int key = min(work, kSchedBuckets - 1);
+    key_sh[u] = (uint16_t)key;
+    atomicAdd(&bucket[key], 1);
+  }
+  __syncthreads();
+  // exclusive scan over the buckets in descending key order: thread t owns
+  // the four buckets 4095-4t .. 4092-4t
+  constexpr int kPer = kSchedBuckets / kSchedThreads;
+  int c[kPer], run = 0;
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) {
+    c[j] = bucket[kSchedBuckets - 1 - (kPer * tid + j)];
+    run += c[j];
+  }
+  int incl = run;  // inclusive scan of `run` over the threads
+  const int lane = tid & 63, wave = tid >> 6;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int y = __shfl_up(incl, off, 64);
+    if (lane >= off) incl += y;
+  }
+  if (lane == 63) wave_tot[wave] = incl;
+  __syncthreads();
+  int base = incl - run;
+  for (int w = 0; w < wave; ++w) base += wave_tot[w];
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) {
+    bucket[kSchedBuckets - 1 - (kPer * tid + j)] = base;
+    base += c[j];
+  }
+  __syncthreads();
+  for (int u = tid; u < n_units; u += kSchedThreads) order[atomicAdd(&bucket[key_sh[u]], 1)] = u;
 }
 
 template <int D, bool PAGED, bool OUT_BF16>
@@ -431,15 +526,29 @@ void pp_launch(const PPParams& p, uint32_t blocks, hipStream_t st) {
 
 bool attn_pp_supported(const AttnArgs& a) { return (a.hq / a.hkv) % 2 == 0; }
 
-cpa_status launch_attn_pp(const AttnArgs& a, bool paged, hipStream_t st) {
+size_t attn_pp_order_bytes(int n_shards, int num_seqs, int max_q) {
+  const int64_t units = cdiv(max_q, kRows) * (int64_t)num_seqs * n_shards;
+  if (units <= 0 || units > kSchedMaxUnits) return 0;
+  return (size_t)cdiv(units * (int64_t)sizeof(int), 256) * 256;
+}
+
+cpa_status launch_attn_pp(const AttnArgs* shards, int n_shards, bool paged, hipStream_t st, void* order_ws,
+                          size_t order_ws_bytes) {
+  if (n_shards < 1 || n_shards > kMaxShards) return fail(CPA_ERR_INVALID_ARG, "partial attention: bad shard count");
+  const AttnArgs& a = shards[0];
   PPParams p{};
   p.q = (const uint16_t*)a.q;
   p.q_pos = a.q_pos;
   p.cu_q = a.cu_q;
-  p.k = (const uint16_t*)a.k;
-  p.v = (const uint16_t*)a.v;
-  p.k_pos = a.k_pos;
-  p.cu_k = a.cu_k;
+  p.n_shards = n_shards;
+  for (int i = 0; i < n_shards; ++i) {
+    p.k[i] = (const uint16_t*)shards[i].k;
+    p.v[i] = (const uint16_t*)shards[i].v;
+    p.k_pos[i] = shards[i].k_pos;
+    p.cu_k[i] = shards[i].cu_k;
+    p.o[i] = shards[i].o;
+    p.lse[i] = shards[i].lse;
+  }
   p.block_table = a.block_table;
   p.max_blocks = a.max_blocks;
   p.local_kv_lens = a.local_kv_lens;
@@ -452,14 +561,18 @@ cpa_status launch_attn_pp(const AttnArgs& a, bool paged, hipStream_t st) {
   p.g = a.hq / a.hkv;
   p.scale_log2 = a.scale * kLog2e;
   p.causal = a.causal;
-  p.o = a.o;
-  p.lse = a.lse;
-  const int64_t n_groups = cdiv(a.max_q, kRows) * a.num_seqs * a.hkv;
+  const int64_t n_groups = cdiv(a.max_q, kRows) * a.num_seqs * n_shards * a.hkv;
   const int64_t blocks = cdiv(n_groups, 8) * 8 * (p.g / 2);
   if (blocks > INT32_MAX) return fail(CPA_ERR_INVALID_ARG, "partial attention: problem too large for one launch");
   p.n_groups = (int)n_groups;
   if (blocks == 0) return CPA_OK;
   const uint32_t nb = (uint32_t)blocks;
+  const size_t order_bytes = paged ? 0 : attn_pp_order_bytes(n_shards, a.num_seqs, a.max_q);
+  if (order_bytes > 0 && order_ws && order_ws_bytes >= order_bytes) {
+    p.order = (const int*)order_ws;
+    const int n_units = (int)(n_groups / a.hkv);
+    hipLaunchKernelGGL(pp_schedule_kernel, dim3(1), dim3(kSchedThreads), 0, st, p, n_units, (int*)order_ws);
+  }
   if (a.d == 64) {
     if (paged) a.o_bf16 ? pp_launch<64, true, true>(p, nb, st) : pp_launch<64, true, false>(p, nb, st);
     else a.o_bf16 ? pp_launch<64, false, true>(p, nb, st) : pp_launch<64, false, false>(p, nb, st);

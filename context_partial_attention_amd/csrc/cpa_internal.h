@@ -61,9 +61,16 @@ struct AttnArgs {
 
 cpa_status launch_attn_f32(const AttnArgs& a, hipStream_t st);
 cpa_status launch_attn_mfma(const AttnArgs& a, bool paged, hipStream_t st);
-// Two-group workgroup for GQA groups of even size (hq / hkv even).
+// Two-group workgroup for GQA groups of even size (hq / hkv even); one launch
+// covers up to kMaxShards contiguous KV shards (a single one when paged),
+// each with its own output. With contiguous shards an optional order
+// workspace of attn_pp_order_bytes() lets a pre-pass run the heaviest tile
+// units first (0 bytes: the problem is too large to sort, index order).
+constexpr int kMaxShards = 8;
 bool attn_pp_supported(const AttnArgs& a);
-cpa_status launch_attn_pp(const AttnArgs& a, bool paged, hipStream_t st);
+size_t attn_pp_order_bytes(int n_shards, int num_seqs, int max_q);
+cpa_status launch_attn_pp(const AttnArgs* shards, int n_shards, bool paged, hipStream_t st,
+                          void* order_ws = nullptr, size_t order_ws_bytes = 0);
 size_t decode_workspace_bytes(int32_t num_seqs, int32_t max_blocks, int32_t block_size, int32_t hq, int32_t d);
 cpa_status launch_attn_decode(const AttnArgs& a, hipStream_t st);
 

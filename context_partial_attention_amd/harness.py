@@ -142,7 +142,11 @@ class Runner:
         self.o = torch.empty((tq, w.hq, w.d), dtype=self.merged_dtype, device=dev)
         self.lse = torch.empty((tq, w.hq), dtype=torch.float32, device=dev)
         self.workspace = None
-        if w.kind != "pass_kv":
+        if w.kind == "pass_kv":
+            need = cpa.partial_attn_multi_workspace(w.cp, len(inp["lens"]), inp["max_q"])
+            if need:
+                self.workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+        else:
             need = max(
                 cpa.partial_attn_paged_workspace(len(inp["lens"]), inp["max_q"], r["block_table"].shape[1],
                                                  w.block_size, w.hq, w.d)
@@ -165,11 +169,25 @@ class Runner:
                                    inp["max_q"], w.scale, True, out=self.o_parts[i], lse=self.lse_parts[i],
                                    workspace=self.workspace, stream=stream)
 
+    def partials_batched(self, stream=None, ordered=True):
+        """Every pass-KV step of the rank in one launch (all shards resident),
+        heaviest tiles first unless `ordered` is False."""
+        inp, w = self.inp, self.w
+        st = inp["steps"]
+        cpa.partial_attn_multi(inp["q"], inp["q_pos"], inp["cu_q"], [s["k"] for s in st], [s["v"] for s in st],
+                               [s["k_pos"] for s in st], [s["cu_k"] for s in st], inp["max_q"], w.scale, True,
+                               outs=self.o_parts, lses=self.lse_parts,
+                               workspace=self.workspace if ordered else None, stream=stream)
+
     def merge(self, stream=None):
         cpa.lse_merge(self.o_parts, self.lse_parts, out=self.o, lse_out=self.lse, stream=stream)
 
     def step(self, stream=None):
-        """The rank's whole share: every partial, then the merge."""
-        for i in range(self.w.cp):
-            self.partial(i, stream)
+        """The rank's whole share: every partial, then the merge. Pass-KV steps
+        run as one batched launch (their shards are all resident)."""
+        if self.w.kind == "pass_kv":
+            self.partials_batched(stream)
+        else:
+            for i in range(self.w.cp):
+                self.partial(i, stream)
         self.merge(stream)

@@ -146,6 +146,41 @@ cpa_status cpa_partial_attn(const void* q, const int32_t* q_pos, const int32_t* 
                             void* stream);
 
 /* ---------------------------------------------------------------------------
+ * cpa_partial_attn_multi — several pass-KV steps in one call: the same Q
+ * shard against n_shards contiguous KV shards that are all resident, one
+ * partial (O, LSE) per shard (device).
+ *
+ * [PASSKV], Purpose: the step partials of pass-KV prefill are independent
+ * computations over disjoint key sets (they only meet in the merge); when the
+ * shards are already resident they can run as one launch. With causal masks
+ * over zigzag shards the work of a query tile differs by an order of
+ * magnitude between tiles and shards; given a workspace, a small pre-pass
+ * orders the launch heaviest tile first, which keeps its tail short. Each
+ * shard's result is exactly what cpa_partial_attn returns for it, whatever
+ * the order.
+ *
+ * In: n_shards in [1, 8]; k, v, k_pos, cu_k, o, lse are HOST arrays of
+ *   n_shards DEVICE pointers with the meaning, layout and constraints of the
+ *   corresponding cpa_partial_attn arguments (k_pos entries may be NULL
+ *   under CPA_MASK_NONE); every other tensor argument is shared by all
+ *   shards. workspace: device memory of workspace_bytes >= the size
+ *   cpa_partial_attn_multi_workspace reports, overwritten by the call; it
+ *   may be NULL (or too small, or the reported size 0), and then the tiles
+ *   run in a fixed order (heaviest query tile of each sequence first).
+ * Errors: as cpa_partial_attn; CPA_ERR_INVALID_ARG for n_shards out of range
+ *   or a NULL pointer array / entry.
+ * ------------------------------------------------------------------------- */
+cpa_status cpa_partial_attn_multi_workspace(int32_t n_shards, int32_t num_seqs, int32_t max_q,
+                                            size_t* bytes);
+cpa_status cpa_partial_attn_multi(int32_t n_shards, const void* q, const int32_t* q_pos,
+                                  const int32_t* cu_q, const void* const* k, const void* const* v,
+                                  const int32_t* const* k_pos, const int32_t* const* cu_k,
+                                  int32_t num_seqs, int32_t max_q, int32_t hq, int32_t hkv,
+                                  int32_t d, cpa_dtype in_dtype, float scale, cpa_mask mask,
+                                  void* const* o, cpa_dtype o_dtype, float* const* lse,
+                                  void* workspace, size_t workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
  * cpa_partial_attn_paged_workspace — bytes of device workspace that
  * cpa_partial_attn_paged needs for these sizes (host, no GPU access).
  * Zero when no workspace is needed (max_q > 1).

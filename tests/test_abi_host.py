@@ -148,3 +148,24 @@ def test_device_call_validation_before_gpu(cpa):
     assert lib.cpa_lse_merge(17, ptrs, ptrs, 1, 10, 128, fake, 1, fake, None) == -1
     assert lib.cpa_lse_merge(2, ptrs, ptrs, 1, 10, 80, fake, 1, fake, None) == -2
     assert lib.cpa_lse_merge(0, ptrs, ptrs, 1, 10, 128, fake, 1, fake, None) == -1
+
+
+def test_multi_shard_call_validation_before_gpu(cpa):
+    lib = cpa.load_library()
+    fake = ctypes.c_void_p(0x1000)  # never dereferenced: validation fails first
+    arr = (ctypes.c_void_p * 9)(*([0x1000] * 9))
+
+    def multi(n, k=arr, mask=1, hkv=2, d=128):
+        return lib.cpa_partial_attn_multi(n, fake, fake, fake, k, arr, arr, arr, 1, 4, 8, hkv, d, 0, 0.1, mask, arr,
+                                          1, arr, None, 0, None)
+
+    assert multi(0) == -1  # no shard
+    assert multi(9) == -1  # more than 8 shards
+    assert multi(2, k=None) == -1  # NULL pointer array
+    assert multi(2, hkv=3) == -1  # hq not a multiple of hkv
+    assert multi(2, d=96) == -2  # unsupported head dim
+    n = ctypes.c_size_t(7)
+    assert lib.cpa_partial_attn_multi_workspace(2, 4, 3700, ctypes.byref(n)) == 0
+    assert n.value >= 29 * 4 * 2 * 4 and n.value % 256 == 0  # one int per (query tile, sequence, shard)
+    assert lib.cpa_partial_attn_multi_workspace(2, 4, 0, ctypes.byref(n)) == 0 and n.value == 0
+    assert lib.cpa_partial_attn_multi_workspace(9, 4, 100, ctypes.byref(n)) == -1

@@ -134,6 +134,40 @@ def test_small_bf16_output_and_no_mask(cpa, wl, harness):
     assert_close(f64(o), f64(l), ro, rl, "no-mask bf16-out")
 
 
+MULTI = [
+    ("cp4_r1_ragged", dict(lengths=(300, 517, 1000), batch=3, len_range=(), cp=4, rank=1)),
+    ("cp3_r2_d64_g1", dict(lengths=(777, 64), batch=2, len_range=(), cp=3, rank=2, hq=4, hkv=4, d=64)),
+    ("cp2_r0_fp32", dict(lengths=(200, 90), batch=2, len_range=(), cp=2, rank=0, dtype=torch.float32)),
+]
+
+
+@pytest.mark.parametrize("name,changes", MULTI, ids=[m[0] for m in MULTI])
+def test_multi_shard_launch_equals_separate_calls(cpa, wl, harness, name, changes):
+    """Every pass-KV step in one batched launch gives, shard by shard, exactly
+    the bits of the separate per-step calls, and both match the oracle."""
+    w = wl.scaled(wl.WORKLOADS["qwen2.5_3b_cp2_rank0"], name=name, seed=300 + len(name), **changes)
+    _say(f"case multi {name}")
+    inp = harness.build(w, device="cuda")
+    run = harness.Runner(inp)
+    for i in range(w.cp):
+        run.partial(i)
+    torch.cuda.synchronize()
+    sep = [(o.clone(), l.clone()) for o, l in zip(run.o_parts, run.lse_parts)]
+    for ordered in (False, True):  # fixed order, then heaviest-tile-first order
+        for o, l in zip(run.o_parts, run.lse_parts):
+            o.fill_(float("nan"))
+            l.fill_(float("nan"))
+        run.partials_batched(ordered=ordered)
+        torch.cuda.synchronize()
+        for s, (o, l) in enumerate(sep):
+            assert torch.equal(run.o_parts[s], o), f"{name} shard {s} ordered={ordered}: O differs from separate call"
+            assert torch.equal(run.lse_parts[s], l), f"{name} shard {s} ordered={ordered}: LSE differs"
+    rows, parts, _ = expected_pass_kv(inp, None)
+    tol = dict(o_tol=1e-4, lse_tol=1e-5) if changes.get("dtype") == torch.float32 else {}
+    for s, (o_ref, l_ref) in enumerate(parts):
+        assert_close(f64(run.o_parts[s]), f64(run.lse_parts[s]), o_ref, l_ref, f"multi {name} shard {s}", **tol)
+
+
 def test_invariants_ones_and_zero_keys(cpa, wl, harness):
     """V = 1 gives O = 1 on every row that sees a key; K = 0 gives
     LSE = ln(#visible keys) exactly enough to check the mask counts."""
