@@ -16,7 +16,9 @@
 // Group 1 runs one phase behind group 0 and every phase ends with a
 // workgroup barrier, so on each SIMD one wave issues MFMAs while the other
 // does its softmax. Both groups see the same rows, hence the same masks and
-// tile counts, so neither waits on the other.
+// tile counts, so neither waits on the other. The wave in phase A raises its
+// issue priority: left to the hardware, the older wave (group 0) wins every
+// conflict and group 1's matrix work stalls behind group 0's softmax.
 //
 // LDS holds two slots; slot t carries K(t), V(t-1) and the key positions of
 // tile t and is read in phases 2t and 2t+1. Its global loads are issued at
@@ -301,10 +303,32 @@ __global__ __launch_bounds__(kThreads, 1) void attn_pp_kernel(PPParams p) {
   // A(t): O += V(t-1)^T P(t-1)^T, then S(t)^T = K(t) Q^T. The bf16 packing of
   // P(t-1) and its row sum run here, under the matrix work, to keep the
   // softmax phase short.
+  //
+  // PV operand i: d-block i % (D/32), k-step i / (D/32) (consecutive MFMAs
+  // accumulate into different d-blocks). QK operand i: key half i % 2, d-step
+  // i / 2 (the two accumulators alternate). When both run, they form one
+  // pipeline of 4 D/32 + D/8 MFMAs whose LDS operands are read kRing MFMAs
+  // ahead from a single register ring, so the first K reads are in flight
+  // while the PV MFMAs run. The row sum of P is a pairwise tree whose adds
+  // are spread over the PV MFMAs.
   auto phase_a = [&](int t) {
+    // the wave feeding the matrix core issues first when both waves of a
+    // SIMD have an instruction ready (by default the older wave would)
+    __builtin_amdgcn_s_setprio(2);
     const int s = t & 1;
-    if (t >= 1 && p_valid) {
-      bf16x8 pb[4];
+    const bool do_pv = t >= 1 && p_valid;
+    const bool do_qk = t < n && __builtin_amdgcn_readfirstlane(kpos_sh[s][0]) <= wave_qmax;
+    const uint16_t* vs = vslot(s) + v_lane;
+    const uint16_t* ks = kslot(s) + k_lane;
+    constexpr int kPV = 4 * (D / 32), kQK = D / 8, kRing = 6;
+    constexpr int kSumPer = (31 + kPV - 1) / kPV;  // row-sum adds per PV MFMA
+    auto vop = [&](int i) {
+      return *(const bf16x8*)(vs + 32 * (i % (D / 32)) * T::kVStride + 16 * (i / (D / 32)));
+    };
+    auto kop = [&](int i) { return *(const bf16x8*)(ks + (i & 1) * 32 * T::kKStride + 16 * (i >> 1)); };
+    bf16x8 pb[4];
+    float sums[31];  // [0, 16): s0[v] + s1[v]; node a >= 16: sums[2(a-16)] + sums[2(a-16)+1]
+    auto pack_p = [&]() {
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         pb[0][e] = (__bf16)s0[e];
@@ -312,57 +336,70 @@ __global__ __launch_bounds__(kThreads, 1) void attn_pp_kernel(PPParams p) {
         pb[2][e] = (__bf16)s1[e];
         pb[3][e] = (__bf16)s1[8 + e];
       }
-      float ps = 0.f;
+    };
+    auto sum_step = [&](int a) {
+      if (a < 16) sums[a] = s0[a] + s1[a];
+      else if (a < 31) sums[a] = sums[2 * (a - 16)] + sums[2 * (a - 16) + 1];
+    };
+    auto pv_mfma = [&](int i, const bf16x8& a) {
+      const int db = i % (D / 32), kst = i / (D / 32);
+      oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[kst], oacc[db], 0, 0, 0);
+    };
+    auto qk_mfma = [&](int i, const bf16x8& a) {
+      if (i & 1) s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[i >> 1], i < 2 ? f32x16{} : s1, 0, 0, 0);
+      else s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[i >> 1], i < 2 ? f32x16{} : s0, 0, 0, 0);
+    };
+    if (do_pv && do_qk) {
+      auto op = [&](int j) { return j < kPV ? vop(j) : kop(j - kPV); };
+      bf16x8 ring[kRing];
 #pragma unroll
-      for (int v = 0; v < 16; ++v) ps += s0[v] + s1[v];
-      l_run += ps;
-      const uint16_t* vs = vslot(s) + v_lane;
-      // operand i = (k-step i / (D/32), d-block i % (D/32)); consecutive MFMAs
-      // accumulate into different d-blocks, and the transposing reads run
-      // kVPre operands ahead
-      constexpr int kOps = 4 * (D / 32), kVPre = 4;
-      auto vop = [&](int i) {
-        return *(const bf16x8*)(vs + 32 * (i % (D / 32)) * T::kVStride + 16 * (i / (D / 32)));
-      };
-      bf16x8 va[kVPre];
+      for (int j = 0; j < kRing; ++j) ring[j] = op(j);
+      pack_p();
 #pragma unroll
-      for (int i = 0; i < kVPre; ++i) va[i] = vop(i);
-#pragma unroll
-      for (int i = 0; i < kOps; ++i) {
+      for (int j = 0; j < kPV + kQK; ++j) {
         __builtin_amdgcn_sched_barrier(0);
-        const int db = i % (D / 32), kst = i / (D / 32);
-        oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[i % kVPre], pb[kst], oacc[db], 0, 0, 0);
-        if (i + kVPre < kOps) va[i % kVPre] = vop(i + kVPre);
-      }
-    }
-    if (t < n && __builtin_amdgcn_readfirstlane(kpos_sh[s][0]) <= wave_qmax) {
-      const uint16_t* ks = kslot(s) + k_lane;
-      s0 = f32x16{};
-      s1 = f32x16{};
-      // K operands read kPre steps ahead of their MFMAs (a ring of registers),
-      // so LDS latency overlaps the matrix work
-      constexpr int kPre = 3;
-      bf16x8 ra[kPre], rb[kPre];
+        if (j < kPV) pv_mfma(j, ring[j % kRing]);
+        else qk_mfma(j - kPV, ring[j % kRing]);
+        if (j + kRing < kPV + kQK) ring[j % kRing] = op(j + kRing);
+        if (j < kPV) {
 #pragma unroll
-      for (int kk = 0; kk < kPre; ++kk) {
-        ra[kk] = *(const bf16x8*)(ks + 16 * kk);
-        rb[kk] = *(const bf16x8*)(ks + 32 * T::kKStride + 16 * kk);
-      }
-#pragma unroll
-      for (int kk = 0; kk < D / 16; ++kk) {
-        __builtin_amdgcn_sched_barrier(0);
-        s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ra[kk % kPre], qf[kk], s0, 0, 0, 0);
-        s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rb[kk % kPre], qf[kk], s1, 0, 0, 0);
-        if (kk + kPre < D / 16) {
-          ra[kk % kPre] = *(const bf16x8*)(ks + 16 * (kk + kPre));
-          rb[kk % kPre] = *(const bf16x8*)(ks + 32 * T::kKStride + 16 * (kk + kPre));
+          for (int u = 0; u < kSumPer; ++u) sum_step(kSumPer * j + u);
         }
+      }
+      l_run += sums[30];
+      return;
+    }
+    if (do_pv) {
+      bf16x8 ring[kRing];
+#pragma unroll
+      for (int j = 0; j < kRing; ++j) ring[j] = vop(j);
+      pack_p();
+#pragma unroll
+      for (int j = 0; j < kPV; ++j) {
+        __builtin_amdgcn_sched_barrier(0);
+        pv_mfma(j, ring[j % kRing]);
+        if (j + kRing < kPV) ring[j % kRing] = vop(j + kRing);
+#pragma unroll
+        for (int u = 0; u < kSumPer; ++u) sum_step(kSumPer * j + u);
+      }
+      l_run += sums[30];
+    }
+    if (do_qk) {
+      bf16x8 ring[kRing];
+#pragma unroll
+      for (int j = 0; j < kRing; ++j) ring[j] = kop(j);
+#pragma unroll
+      for (int j = 0; j < kQK; ++j) {
+        __builtin_amdgcn_sched_barrier(0);
+        qk_mfma(j, ring[j % kRing]);
+        if (j + kRing < kQK) ring[j % kRing] = kop(j + kRing);
       }
     }
   };
 
   // B(t): mask and online softmax of S(t) -> P(t) (fp32, in place)
   auto phase_b = [&](int t) {
+    __builtin_amdgcn_s_setprio(0);
     const int* kp = kpos_sh[t & 1];
     p_valid = __builtin_amdgcn_readfirstlane(kp[0]) <= wave_qmax;
     if (!p_valid) return;
