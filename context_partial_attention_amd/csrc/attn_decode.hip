@@ -100,26 +100,43 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecParams p) {
     for (int e = 0; e < 8; ++e) acc[h][e] = 0.f;
 
   const int64_t head_stride = 16LL * D;  // one (block, kv head) slab
-  for (int b = b_begin + wave; b < b_end; b += kWaves) {
-    const int phys = p.block_table[(int64_t)seq * p.max_blocks + b];
+  // This wave's blocks are b_begin + wave + kWaves*i, i < nb (at most
+  // kBlocksPerWave); lane i holds the physical block of the i-th, read once.
+  constexpr int kBlocksPerWave = kSplit / 16 / kWaves;
+  static_assert(kBlocksPerWave <= 64, "one block-table entry per lane");
+  const int first_b = b_begin + wave;
+  const int nb = first_b < b_end ? (b_end - first_b + kWaves - 1) / kWaves : 0;
+  const int phys_lane =
+      lane < nb ? p.block_table[(int64_t)seq * p.max_blocks + first_b + kWaves * lane] : 0;
+
+  // K and V of a block in registers; the next block's loads are issued before
+  // the current block is computed, so HBM latency overlaps the math
+  struct Blk {
+    bf16x8 ka[D / 32];
+    u32x4 vr[kKPL];
+  };
+  auto load_blk = [&](int i, Blk& r) {
+    const int b = first_b + kWaves * i;
+    const int phys = __builtin_amdgcn_readlane(phys_lane, i);
     const int nvalid = min(16, k_end - b * 16);
     const int64_t slab = ((int64_t)phys * p.hkv + kvh) * head_stride;
     const uint16_t* kb = p.kc + slab;
     const uint16_t* vb = p.vc + slab;
-    bf16x8 ka[D / 32];
     const int krow = min(n, nvalid - 1);
 #pragma unroll
-    for (int kk = 0; kk < D / 32; ++kk) ka[kk] = *(const bf16x8*)(kb + krow * D + 32 * kk + 8 * ks);
-    u32x4 vr[kKPL];
+    for (int kk = 0; kk < D / 32; ++kk) r.ka[kk] = *(const bf16x8*)(kb + krow * D + 32 * kk + 8 * ks);
 #pragma unroll
-    for (int i = 0; i < kKPL; ++i) vr[i] = *(const u32x4*)(vb + min(kg * kKPL + i, nvalid - 1) * D + 8 * dc);
-
+    for (int i2 = 0; i2 < kKPL; ++i2) r.vr[i2] = *(const u32x4*)(vb + min(kg * kKPL + i2, nvalid - 1) * D + 8 * dc);
+  };
+  auto compute_blk = [&](int i, const Blk& r) {
+    const int b = first_b + kWaves * i;
+    const int nvalid = min(16, k_end - b * 16);
     f32x4 s = {};
 #pragma unroll
-    for (int kk = 0; kk < D / 32; ++kk) s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[kk], qf[kk], s, 0, 0, 0);
+    for (int kk = 0; kk < D / 32; ++kk) s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(r.ka[kk], qf[kk], s, 0, 0, 0);
     // s[i]: key 4*ks + i of this block, head column n
 #pragma unroll
-    for (int i = 0; i < 4; ++i) s[i] = (4 * ks + i < nvalid) ? s[i] * sl2 : kNegInf;
+    for (int j = 0; j < 4; ++j) s[j] = (4 * ks + j < nvalid) ? s[j] * sl2 : kNegInf;
     float mx = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
     mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
     mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
@@ -127,7 +144,7 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecParams p) {
     const float base = (m_new == kNegInf) ? 0.f : m_new;
     const float alpha = hw_exp2(m_run - base);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) s[i] = hw_exp2(s[i] - base);
+    for (int j = 0; j < 4; ++j) s[j] = hw_exp2(s[j] - base);
     l_run = l_run * alpha + (s[0] + s[1]) + (s[2] + s[3]);
     m_run = m_new;
     if (n < HC) {
@@ -135,31 +152,39 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecParams p) {
       if (ks == 0) a_sh[wave][n] = alpha;
     }
     __builtin_amdgcn_wave_barrier();
-    float vf[kKPL][8];
-#pragma unroll
-    for (int i = 0; i < kKPL; ++i)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        vf[i][2 * e] = bf16_lo(vr[i][e]);
-        vf[i][2 * e + 1] = bf16_hi(vr[i][e]);
-      }
+    // acc[h][e] = acc[h][e] * alpha[h] + sum over this lane's keys of p[h][key] v[key][8 dc + e]
+    // (heads past nh carry zero queries; their sums are never written)
+    float pv[HC][kKPL];
 #pragma unroll
     for (int h = 0; h < HC; ++h) {
-      if (h < nh) {
-        const float al = a_sh[wave][h];
-        float pv[kKPL];
+      const float al = a_sh[wave][h];
 #pragma unroll
-        for (int i = 0; i < kKPL; ++i) pv[i] = p_sh[wave][h][kg * kKPL + i];
+      for (int e = 0; e < 8; ++e) acc[h][e] *= al;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          float x = acc[h][e] * al;
+      for (int i2 = 0; i2 < kKPL; ++i2) pv[h][i2] = p_sh[wave][h][kg * kKPL + i2];
+    }
 #pragma unroll
-          for (int i = 0; i < kKPL; ++i) x = fmaf(pv[i], vf[i][e], x);
-          acc[h][e] = x;
+    for (int i2 = 0; i2 < kKPL; ++i2)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float lo = bf16_lo(r.vr[i2][e]), hi = bf16_hi(r.vr[i2][e]);
+#pragma unroll
+        for (int h = 0; h < HC; ++h) {
+          acc[h][2 * e] = fmaf(pv[h][i2], lo, acc[h][2 * e]);
+          acc[h][2 * e + 1] = fmaf(pv[h][i2], hi, acc[h][2 * e + 1]);
         }
       }
-    }
     __builtin_amdgcn_wave_barrier();
+  };
+  Blk bufa, bufb;
+  if (nb > 0) load_blk(0, bufa);
+  for (int i = 0; i < nb; i += 2) {
+    if (i + 1 < nb) load_blk(i + 1, bufb);
+    compute_blk(i, bufa);
+    if (i + 1 < nb) {
+      if (i + 2 < nb) load_blk(i + 2, bufa);
+      compute_blk(i + 1, bufb);
+    }
   }
 
   // reduce over the key subsets of the wave
