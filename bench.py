@@ -107,26 +107,34 @@ def bench_workload(name: str, steps: int, warmup: int) -> dict:
     torch.cuda.synchronize()
 
     ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
-    part_ev = [[(ev(), ev()) for _ in launches] for _ in range(steps)]
-    merge_ev = [(ev(), ev()) for _ in range(steps)]
+    # (1) the step: events only at the two ends of the timed region (an event
+    # recorded between two kernels opens a dispatch gap of ~10 us on the stream)
     g0, g1 = ev(), ev()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     g0.record(stream)
-    for k in range(steps):
-        for j, f in enumerate(launches):
-            part_ev[k][j][0].record(stream)
+    for _ in range(steps):
+        for f in launches:
             f()
-            part_ev[k][j][1].record(stream)
-        merge_ev[k][0].record(stream)
         run.merge()
-        merge_ev[k][1].record(stream)
     g1.record(stream)
     torch.cuda.synchronize()
     wall_ms = (time.perf_counter() - t0) * 1e3
     gpu_ms = g0.elapsed_time(g1)
-    part_ms = [[a.elapsed_time(b) for a, b in row] for row in part_ev]
-    mrg_ms = [a.elapsed_time(b) for a, b in merge_ev]
+    # (2) each launch of the step on its own: `steps` back-to-back launches
+    # between one pair of events on the launch stream, mean per launch
+    def per_launch_ms(f):
+        a, b = ev(), ev()
+        torch.cuda.synchronize()
+        a.record(stream)
+        for _ in range(steps):
+            f()
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / steps
+
+    part_ms = [per_launch_ms(f) for f in launches]
+    merge_ms = per_launch_ms(run.merge)
 
     rows = inp["q"].shape[0] * w.hq
     mbytes = merge_bytes(w, rows, w.cp, 2 if run.merged_dtype == torch.bfloat16 else 4)
@@ -136,10 +144,10 @@ def bench_workload(name: str, steps: int, warmup: int) -> dict:
         "steps": steps,
         "ms_per_step": wall_ms / steps,
         "gpu_ms_per_step": gpu_ms / steps,
-        "partial_ms": [float(np.mean([r[j] for r in part_ms])) for j in range(len(launches))],
-        "merge_ms": float(np.mean(mrg_ms)),
-        "merge_GBps": mbytes / (np.mean(mrg_ms) * 1e-3) / 1e9,
-        "merge_hbm_frac": mbytes / (np.mean(mrg_ms) * 1e-3) / 1e9 / PEAK_HBM_GBS,
+        "partial_ms": part_ms,
+        "merge_ms": merge_ms,
+        "merge_GBps": mbytes / (merge_ms * 1e-3) / 1e9,
+        "merge_hbm_frac": mbytes / (merge_ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
     }
     if w.kind == "pass_kv":
         pairs = [pass_kv_pairs(inp, i) for i in own]
@@ -151,8 +159,7 @@ def bench_workload(name: str, steps: int, warmup: int) -> dict:
     if w.kind in ("pass_kv", "pass_q"):
         res["TFLOPs"] = sum(flops) / (res["ms_per_step"] * 1e-3) / 1e12
         res["pct_bf16_peak"] = 100 * res["TFLOPs"] / PEAK_BF16_TFLOPS
-        tot_part_ms = sum(sum(r) for r in part_ms)
-        res["partial_TFLOPs"] = sum(flops) * steps / (tot_part_ms * 1e-3) / 1e12
+        res["partial_TFLOPs"] = sum(flops) / (sum(part_ms) * 1e-3) / 1e12
         res["partial_pct_bf16_peak"] = 100 * res["partial_TFLOPs"] / PEAK_BF16_TFLOPS
     else:
         # decode: K and V of every visible local token, q, O (fp32) and LSE
@@ -259,8 +266,8 @@ def cpu_baseline(name: str, budget_s: float = 10.0) -> dict:
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=10)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workloads", type=str, default=",".join(DEFAULT_WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
