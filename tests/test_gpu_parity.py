@@ -139,6 +139,8 @@ MULTI = [
     ("cp3_r2_d64_g1", dict(lengths=(777, 64), batch=2, len_range=(), cp=3, rank=2, hq=4, hkv=4, d=64)),
     ("cp2_r0_fp32", dict(lengths=(200, 90), batch=2, len_range=(), cp=2, rank=0, dtype=torch.float32)),
     ("cp2_r1_d64_g4", dict(lengths=(600, 129), batch=2, len_range=(), cp=2, rank=1, hq=8, hkv=2, d=64)),
+    # eight shards (the most one launch takes), sequences shorter than 2cp: empty chunks and shards
+    ("cp8_r5_tiny", dict(lengths=(3, 0, 17, 250, 1), batch=5, len_range=(), cp=8, rank=5)),
 ]
 
 
