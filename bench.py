@@ -176,6 +176,13 @@ def bench_workload(name: str, steps: int, warmup: int) -> dict:
         del rk
     if w.kind == "pass_kv":
         res["seq_lens"] = inp["lens"]
+        if w.dtype == torch.bfloat16 and (w.hq // w.hkv) % 2 == 0:
+            # next row (fused merge): every resident shard walked in one launch,
+            # the merged (O, LSE) written directly; same algorithmic work
+            fw_ms = per_launch_ms(run.merged_walk)
+            res["fused_walk_ms"] = fw_ms
+            res["fused_walk_TFLOPs"] = sum(flops) / (fw_ms * 1e-3) / 1e12
+            res["fused_walk_pct_bf16_peak"] = 100 * res["fused_walk_TFLOPs"] / PEAK_BF16_TFLOPS
     del run, inp
     torch.cuda.empty_cache()
     return res
@@ -345,6 +352,13 @@ def main():
             "flops_per_launch": flops_per_launch,
         },
         "workloads": {k: v for k, v in results.items() if k != HEADLINE},
+        # not the step above: the fused-merge walk (cpa_partial_attn_merged) on
+        # the same workload, merged output without fp32 partials or a merge pass
+        "fused_merge": {
+            "ms": h.get("fused_walk_ms"),
+            "TFLOPs": h.get("fused_walk_TFLOPs"),
+            "pct_bf16_peak": h.get("fused_walk_pct_bf16_peak"),
+        },
     }
     if not args.no_cpu_baseline:
         log("[bench] cpu baseline (oracle) ...")

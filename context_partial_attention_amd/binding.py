@@ -64,6 +64,10 @@ def load_library():
                                            ctypes.POINTER(_p), ctypes.POINTER(_p), _i32, _i32, _i32, _i32, _i32,
                                            _i32, _f32, _i32, ctypes.POINTER(_p), _i32, ctypes.POINTER(_p), _p,
                                            ctypes.c_size_t, _p]
+    lib.cpa_partial_attn_merged.restype = _i32
+    lib.cpa_partial_attn_merged.argtypes = [_i32, _p, _p, _p, ctypes.POINTER(_p), ctypes.POINTER(_p),
+                                            ctypes.POINTER(_p), ctypes.POINTER(_p), _i32, _i32, _i32, _i32, _i32,
+                                            _i32, _f32, _i32, _p, _i32, _p, _p, ctypes.c_size_t, _p]
     lib.cpa_partial_attn_paged_workspace.restype = _i32
     lib.cpa_partial_attn_paged_workspace.argtypes = [_i32, _i32, _i32, _i32, _i32, _i32,
                                                      ctypes.POINTER(ctypes.c_size_t)]
@@ -216,6 +220,32 @@ def partial_attn_multi(q, q_pos, cu_q, ks, vs, k_poss, cu_ks, max_q: int, scale:
         _dev(workspace, "workspace"), 0 if workspace is None else workspace.numel() * workspace.element_size(),
         _stream(stream)))
     return outs, lses
+
+
+def partial_attn_merged(q, q_pos, cu_q, ks, vs, k_poss, cu_ks, max_q: int, scale: float, causal: bool = True,
+                        out=None, lse=None, out_dtype=None, workspace=None, stream=None):
+    """The merged pass-KV result over resident shards (ks[i], vs[i], k_poss[i], cu_ks[i]) in one walk.
+    `workspace` as for partial_attn_multi. Returns (o, lse)."""
+    torch = _torch()
+    tq, hq, d = q.shape
+    n = len(ks)
+    hkv = ks[0].shape[1]
+    out_dtype = out_dtype or torch.float32
+    if out is None:
+        out = torch.empty((tq, hq, d), dtype=out_dtype, device=q.device)
+    if lse is None:
+        lse = torch.empty((tq, hq), dtype=torch.float32, device=q.device)
+    if not (len(vs) == len(k_poss) == len(cu_ks) == n):
+        raise ValueError("every per-shard list needs one entry per shard")
+    arr = lambda ts, name: (_p * n)(*[_dev(t, name) for t in ts])  # noqa: E731
+    num_seqs = cu_q.numel() - 1
+    _check("cpa_partial_attn_merged", load_library().cpa_partial_attn_merged(
+        n, _dev(q, "q"), _dev(q_pos, "q_pos"), _dev(cu_q, "cu_q"), arr(ks, "k"), arr(vs, "v"), arr(k_poss, "k_pos"),
+        arr(cu_ks, "cu_k"), num_seqs, int(max_q), hq, hkv, d, _dtype_code(q), float(scale),
+        MASK_CAUSAL if causal else MASK_NONE, _dev(out, "out"), _dtype_code(out), _dev(lse, "lse"),
+        _dev(workspace, "workspace"), 0 if workspace is None else workspace.numel() * workspace.element_size(),
+        _stream(stream)))
+    return out, lse
 
 
 def partial_attn_paged_workspace(num_seqs: int, max_q: int, max_blocks: int, block_size: int, hq: int,

@@ -135,6 +135,57 @@ extern "C" cpa_status cpa_partial_attn_multi(int32_t n_shards, const void* q, co
   return CPA_OK;
 }
 
+extern "C" cpa_status cpa_partial_attn_merged(int32_t n_shards, const void* q, const int32_t* q_pos,
+                                              const int32_t* cu_q, const void* const* k, const void* const* v,
+                                              const int32_t* const* k_pos, const int32_t* const* cu_k,
+                                              int32_t num_seqs, int32_t max_q, int32_t hq, int32_t hkv, int32_t d,
+                                              cpa_dtype in_dtype, float scale, cpa_mask mask, void* o,
+                                              cpa_dtype o_dtype, float* lse, void* workspace, size_t workspace_bytes,
+                                              void* stream) {
+  const char* fn = "cpa_partial_attn_merged";
+  if (n_shards < 1 || n_shards > kMaxShards)
+    return fail(CPA_ERR_INVALID_ARG, "%s: n_shards %d not in [1, %d]", fn, n_shards, kMaxShards);
+  if (!k || !v || !cu_k || (mask == CPA_MASK_CAUSAL && !k_pos))
+    return fail(CPA_ERR_INVALID_ARG, "%s: NULL pointer array", fn);
+  if (in_dtype != CPA_BF16 && in_dtype != CPA_F32) return fail(CPA_ERR_INVALID_ARG, "%s: bad in_dtype", fn);
+  if (o_dtype != CPA_BF16 && o_dtype != CPA_F32) return fail(CPA_ERR_INVALID_ARG, "%s: bad o_dtype", fn);
+  AttnArgs args[kMaxShards];
+  for (int i = 0; i < n_shards; ++i) {
+    const int32_t* kp = (mask == CPA_MASK_CAUSAL) ? k_pos[i] : nullptr;
+    cpa_status st = check_common(fn, q, q_pos, cu_q, k[i], v[i], num_seqs, max_q, hq, hkv, d, scale, mask, o, lse);
+    if (st != CPA_OK) return st;
+    if (num_seqs > 0 && max_q > 0) {
+      if (!cu_k[i]) return fail(CPA_ERR_INVALID_ARG, "%s: cu_k[%d] is NULL", fn, i);
+      if (mask == CPA_MASK_CAUSAL && !kp) return fail(CPA_ERR_INVALID_ARG, "%s: k_pos[%d] is NULL", fn, i);
+    }
+    AttnArgs& a = args[i];
+    a.q = q;
+    a.q_pos = q_pos;
+    a.cu_q = cu_q;
+    a.k = k[i];
+    a.v = v[i];
+    a.k_pos = kp;
+    a.cu_k = cu_k[i];
+    a.num_seqs = num_seqs;
+    a.max_q = max_q;
+    a.hq = hq;
+    a.hkv = hkv;
+    a.d = d;
+    a.scale = scale;
+    a.causal = mask == CPA_MASK_CAUSAL;
+    a.o = o;
+    a.o_bf16 = o_dtype == CPA_BF16;
+    a.lse = lse;
+  }
+  if (in_dtype != CPA_BF16 || !attn_pp_supported(args[0]))
+    return fail(CPA_ERR_UNSUPPORTED, "%s: needs bf16 inputs and an even GQA group (hq / hkv)", fn);
+  cpa_status st = check_device();
+  if (st != CPA_OK) return st;
+  if (num_seqs == 0 || max_q == 0) return CPA_OK;
+  const MergedOut out{o, o_dtype == CPA_BF16, lse};
+  return launch_attn_pp(args, n_shards, /*paged=*/false, (hipStream_t)stream, workspace, workspace_bytes, &out);
+}
+
 extern "C" cpa_status cpa_partial_attn_paged_workspace(int32_t num_seqs, int32_t max_q, int32_t max_blocks,
                                                        int32_t block_size, int32_t hq, int32_t d, size_t* bytes) {
   const char* fn = "cpa_partial_attn_paged_workspace";

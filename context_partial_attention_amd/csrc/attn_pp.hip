@@ -107,7 +107,7 @@ __device__ int pp_count_le(const int* __restrict__ a, int n, int x) {
   }
 }
 
-template <int D, bool PAGED, bool OUT_BF16>
+template <int D, bool PAGED, bool OUT_BF16, bool MERGED>
 __global__ __launch_bounds__(kThreads, 1) void attn_pp_kernel(PPParams p) {
   using T = PPTile<D>;
   __shared__ __attribute__((aligned(16))) uint16_t smem[2 * T::kSlotElems];
@@ -125,17 +125,16 @@ __global__ __launch_bounds__(kThreads, 1) void attn_pp_kernel(PPParams p) {
   if constexpr (!PAGED) {
     if (p.order) grp = p.order[grp / p.hkv] * p.hkv + grp % p.hkv;
   }
-  // group = ((tile_desc * num_seqs + seq) * n_shards + shard) * hkv + kvh:
-  // the heaviest query tiles of every sequence and shard come first
+  // group = ((tile_desc * num_seqs + seq) * n_shards + shard) * hkv + kvh
+  // (no shard term when MERGED: one group walks every shard): the heaviest
+  // query tiles of every sequence and shard come first
+  const int n_sh_grid = MERGED ? 1 : p.n_shards;
   const int kvh = grp % p.hkv;
   const int t2 = grp / p.hkv;
-  const int shard = t2 % p.n_shards;
-  const int t3 = t2 / p.n_shards;
+  const int shard = t2 % n_sh_grid;
+  const int t3 = t2 / n_sh_grid;
   const int seq = t3 % p.num_seqs;
   const int t_desc = t3 / p.num_seqs;
-  const uint16_t* __restrict__ kmat = p.k[shard];
-  const uint16_t* __restrict__ vmat = p.v[shard];
-  const int* __restrict__ kposv = p.k_pos[shard];
   const int qa = p.cu_q[seq], qe = p.cu_q[seq + 1];
   const int n_tiles = (qe - qa + kRows - 1) / kRows;
   if (t_desc >= n_tiles) return;
@@ -165,21 +164,64 @@ __global__ __launch_bounds__(kThreads, 1) void attn_pp_kernel(PPParams p) {
     blk_qmax = INT_MAX - 1;
   }
 
-  // ---- key range [ka, n_end) some row of the workgroup can see
-  int ka, ke;
-  if constexpr (PAGED) {
-    ka = 0;
-    ke = min(p.local_kv_lens[seq], p.max_blocks * 16);  // never index past the block table
+  // ---- key segments: the workgroup's own shard, or (MERGED) every shard in
+  // turn. A segment holds the keys [ka, end) of its shard that some row of
+  // the workgroup can see; its 64-key tiles are consecutive tiles of the
+  // walk. One online softmax runs over the whole walk, so a MERGED workgroup
+  // ends with the exact merge of the shards' partials.
+  __shared__ int seg_sh[MERGED ? kMaxShards : 1][3];  // ka, end, first tile of the walk
+  auto seg_range = [&](int sh, int& ka, int& ke) {
+    if constexpr (PAGED) {
+      ka = 0;
+      ke = min(p.local_kv_lens[seq], p.max_blocks * 16);  // never index past the block table
+      if (p.causal) ke = min(ke, rr_count_below(blk_qmax + 1, p.cp, p.rank, p.il));
+    } else {
+      ka = p.cu_k[sh][seq];
+      ke = p.cu_k[sh][seq + 1];
+      if (p.causal) ke = ka + pp_count_le(p.k_pos[sh] + ka, ke - ka, blk_qmax);
+    }
+  };
+  int seg0_ka = 0, seg0_end = 0, n = 0;  // n: tiles of the walk
+  if constexpr (!MERGED) {
+    seg_range(shard, seg0_ka, seg0_end);
+    n = seg0_end > seg0_ka ? (seg0_end - seg0_ka + kBN - 1) / kBN : 0;
   } else {
-    ka = p.cu_k[shard][seq];
-    ke = p.cu_k[shard][seq + 1];
+    for (int sg = 0; sg < p.n_shards; ++sg) {
+      int ka, ke;
+      seg_range(sg, ka, ke);
+      if (tid == 0) {
+        seg_sh[sg][0] = ka;
+        seg_sh[sg][1] = ke;
+        seg_sh[sg][2] = n;
+      }
+      n += ke > ka ? (ke - ka + kBN - 1) / kBN : 0;
+    }
+    __syncthreads();
   }
-  int n_end = ke;
-  if (p.causal) {
-    if constexpr (PAGED) n_end = min(ke, rr_count_below(blk_qmax + 1, p.cp, p.rank, p.il));
-    else n_end = ka + pp_count_le(kposv + ka, ke - ka, blk_qmax);
-  }
-  const int n = n_end > ka ? (n_end - ka + kBN - 1) / kBN : 0;  // tiles
+  // tile t of the walk: its shard's K, V and positions, first key index, end of the visible keys
+  struct TileRef {
+    const uint16_t* k;
+    const uint16_t* v;
+    const int* kp;
+    int j0, end;
+  };
+  // MERGED: a cursor over the segments that only moves forward (tiles are
+  // staged in walk order), so each tile costs one comparison
+  int cur_sg = -1, cur_ka = 0, cur_end = 0, cur_base = 0, cur_next = 0;
+  auto tile_ref = [&](int t) -> TileRef {
+    if constexpr (!MERGED) {
+      return TileRef{p.k[shard], p.v[shard], p.k_pos[shard], seg0_ka + t * kBN, seg0_end};
+    } else {
+      while (t >= cur_next) {
+        ++cur_sg;
+        cur_ka = __builtin_amdgcn_readfirstlane(seg_sh[cur_sg][0]);
+        cur_end = __builtin_amdgcn_readfirstlane(seg_sh[cur_sg][1]);
+        cur_base = __builtin_amdgcn_readfirstlane(seg_sh[cur_sg][2]);
+        cur_next = cur_sg + 1 < p.n_shards ? __builtin_amdgcn_readfirstlane(seg_sh[cur_sg + 1][2]) : INT_MAX;
+      }
+      return TileRef{p.k[cur_sg], p.v[cur_sg], p.k_pos[cur_sg], cur_ka + (t - cur_base) * kBN, cur_end};
+    }
+  };
 
   // ---- Q^T fragments
   bf16x8 qf[D / 16];
@@ -201,8 +243,9 @@ __global__ __launch_bounds__(kThreads, 1) void attn_pp_kernel(PPParams p) {
     if constexpr (PAGED) off[i] = (uint32_t)((r & 15) * D + c8 * 8);
     else off[i] = (uint32_t)(r * row_stride + c8 * 8);
   }
-  auto load_tile = [&](const uint16_t* __restrict__ src, int t, u32x4* regs) {
-    const int j0 = ka + t * kBN;
+  auto load_k = [&](const TileRef& tr, u32x4* regs) {
+    const uint16_t* __restrict__ src = tr.k;
+    const int j0 = tr.j0, n_end = tr.end;
     const bool last = j0 + kBN > n_end;
     if constexpr (PAGED) {
       const int64_t slab = (int64_t)p.hkv * 16 * D;
@@ -231,9 +274,10 @@ __global__ __launch_bounds__(kThreads, 1) void attn_pp_kernel(PPParams p) {
   };
   // V piece of thread tid < kVUnits: keys 2 kp, 2 kp + 1 of the tile, dims 8 dc .. 8 dc + 7
   const int v_kp = tid % (kBN / 2), v_dc = tid / (kBN / 2);
-  auto load_v = [&](int t, u32x4* regs) {
+  auto load_v = [&](const TileRef& tr, u32x4* regs) {
     if (tid >= T::kVUnits) return;
-    const int j0 = ka + t * kBN;
+    const uint16_t* __restrict__ vmat = tr.v;
+    const int j0 = tr.j0, n_end = tr.end;
 #pragma unroll
     for (int r = 0; r < 2; ++r) {
       const int j = min(j0 + 2 * v_kp + r, n_end - 1);
@@ -245,11 +289,11 @@ __global__ __launch_bounds__(kThreads, 1) void attn_pp_kernel(PPParams p) {
       }
     }
   };
-  auto key_pos = [&](int t) -> int {  // position of key tid of tile t (tid < 64), INT_MAX past the end
-    const int j = ka + t * kBN + tid;
-    if (j >= n_end) return INT_MAX;
+  auto key_pos = [&](const TileRef& tr) -> int {  // position of key tid of the tile (tid < 64), INT_MAX past the end
+    const int j = tr.j0 + tid;
+    if (j >= tr.end) return INT_MAX;
     if constexpr (PAGED) return rr_global_pos(j, p.cp, p.rank, p.il);
-    else return p.causal ? kposv[j] : 0;
+    else return p.causal ? tr.kp[j] : 0;
   };
   auto kslot = [&](int s) { return smem + s * T::kSlotElems; };
   auto vslot = [&](int s) { return smem + s * T::kSlotElems + T::kKElems; };
@@ -262,12 +306,18 @@ __global__ __launch_bounds__(kThreads, 1) void attn_pp_kernel(PPParams p) {
   u32x4 kreg[T::kChunks], vreg[2];
   int kp_reg = INT_MAX;
   // slot t = {K(t), V(t-1), positions of tile t}
+  // slots are loaded for t = 0, 1, ..., n in order; the V of a slot is the
+  // previous tile's, whose reference the last call kept
+  TileRef prev_tr{};
   auto load_slot = [&](int t) {
+    TileRef tr{};
     if (t < n) {
-      load_tile(kmat, t, kreg);
-      if (tid < kBN) kp_reg = key_pos(t);
+      tr = tile_ref(t);
+      load_k(tr, kreg);
+      if (tid < kBN) kp_reg = key_pos(tr);
     }
-    if (t >= 1) load_v(t - 1, vreg);
+    if (t >= 1) load_v(MERGED ? prev_tr : tile_ref(t - 1), vreg);
+    prev_tr = tr;
   };
   auto store_slot = [&](int t) {
     const int s = t & 1;
@@ -487,37 +537,43 @@ constexpr int kSchedThreads = 1024;
 constexpr int kSchedBuckets = 4096;
 constexpr int kSchedMaxUnits = 8192;
 
-__global__ __launch_bounds__(kSchedThreads) void pp_schedule_kernel(PPParams p, int n_units, int* order) {
+__global__ __launch_bounds__(kSchedThreads) void pp_schedule_kernel(PPParams p, int n_units, int merged,
+                                                                     int* order) {
   __shared__ int bucket[kSchedBuckets];
   __shared__ uint16_t key_sh[kSchedMaxUnits];
   __shared__ int wave_tot[kSchedThreads / 64];
   const int tid = threadIdx.x;
   for (int b = tid; b < kSchedBuckets; b += kSchedThreads) bucket[b] = 0;
   __syncthreads();
+  // a unit is (tile_desc, seq, shard), or (tile_desc, seq) when merged (its
+  // work is then summed over the shards it walks)
+  const int n_sh_unit = merged ? 1 : p.n_shards;
   for (int u = tid; u < n_units; u += kSchedThreads) {
-    const int shard = u % p.n_shards;
-    const int t3 = u / p.n_shards;
+    const int t3 = u / n_sh_unit;
     const int seq = t3 % p.num_seqs;
     const int t_desc = t3 / p.num_seqs;
     const int qa = p.cu_q[seq], qe = p.cu_q[seq + 1];
     const int n_tiles = (qe - qa + kRows - 1) / kRows;
     int work = 0;
     if (t_desc < n_tiles) {
-      const int ka = p.cu_k[shard][seq], ke = p.cu_k[shard][seq + 1];
-      const int nk = (ke - ka + kBN - 1) / kBN;
-      if (!p.causal) {
-        work = nk;
-      } else {
-        const int row0 = qa + (n_tiles - 1 - t_desc) * kRows;
-        const int qmax = p.q_pos[min(row0 + kRows - 1, qe - 1)];
-        const int* kp = p.k_pos[shard] + ka;
-        int lo = 0, hi = nk;  // key tiles whose first key is visible: [0, lo)
-        while (lo < hi) {
-          const int mid = (lo + hi) >> 1;
-          if (kp[mid * kBN] <= qmax) lo = mid + 1;
-          else hi = mid;
+      const int row0 = qa + (n_tiles - 1 - t_desc) * kRows;
+      const int qmax = p.causal ? p.q_pos[min(row0 + kRows - 1, qe - 1)] : 0;
+      const int sh0 = merged ? 0 : u % p.n_shards, sh1 = merged ? p.n_shards : sh0 + 1;
+      for (int shard = sh0; shard < sh1; ++shard) {
+        const int ka = p.cu_k[shard][seq], ke = p.cu_k[shard][seq + 1];
+        const int nk = (ke - ka + kBN - 1) / kBN;
+        if (!p.causal) {
+          work += nk;
+        } else {
+          const int* kp = p.k_pos[shard] + ka;
+          int lo = 0, hi = nk;  // key tiles whose first key is visible: [0, lo)
+          while (lo < hi) {
+            const int mid = (lo + hi) >> 1;
+            if (kp[mid * kBN] <= qmax) lo = mid + 1;
+            else hi = mid;
+          }
+          work += lo;
         }
-        work = lo;
       }
     }
     const int key = min(work, kSchedBuckets - 1);
@@ -554,9 +610,9 @@ __global__ __launch_bounds__(kSchedThreads) void pp_schedule_kernel(PPParams p, 
   for (int u = tid; u < n_units; u += kSchedThreads) order[atomicAdd(&bucket[key_sh[u]], 1)] = u;
 }
 
-template <int D, bool PAGED, bool OUT_BF16>
+template <int D, bool PAGED, bool OUT_BF16, bool MERGED = false>
 void pp_launch(const PPParams& p, uint32_t blocks, hipStream_t st) {
-  hipLaunchKernelGGL((attn_pp_kernel<D, PAGED, OUT_BF16>), dim3(blocks), dim3(kThreads), 0, st, p);
+  hipLaunchKernelGGL((attn_pp_kernel<D, PAGED, OUT_BF16, MERGED>), dim3(blocks), dim3(kThreads), 0, st, p);
 }
 
 }  // namespace
@@ -570,7 +626,8 @@ size_t attn_pp_order_bytes(int n_shards, int num_seqs, int max_q) {
 }
 
 cpa_status launch_attn_pp(const AttnArgs* shards, int n_shards, bool paged, hipStream_t st, void* order_ws,
-                          size_t order_ws_bytes) {
+                          size_t order_ws_bytes, const MergedOut* merged) {
+  if (merged && paged) return fail(CPA_ERR_INVALID_ARG, "partial attention: a merged walk needs contiguous shards");
   if (n_shards < 1 || n_shards > kMaxShards) return fail(CPA_ERR_INVALID_ARG, "partial attention: bad shard count");
   const AttnArgs& a = shards[0];
   PPParams p{};
@@ -586,6 +643,10 @@ cpa_status launch_attn_pp(const AttnArgs* shards, int n_shards, bool paged, hipS
     p.o[i] = shards[i].o;
     p.lse[i] = shards[i].lse;
   }
+  if (merged) {  // one output: the exact merge over all shards
+    p.o[0] = merged->o;
+    p.lse[0] = merged->lse;
+  }
   p.block_table = a.block_table;
   p.max_blocks = a.max_blocks;
   p.local_kv_lens = a.local_kv_lens;
@@ -598,7 +659,7 @@ cpa_status launch_attn_pp(const AttnArgs* shards, int n_shards, bool paged, hipS
   p.g = a.hq / a.hkv;
   p.scale_log2 = a.scale * kLog2e;
   p.causal = a.causal;
-  const int64_t n_groups = cdiv(a.max_q, kRows) * a.num_seqs * n_shards * a.hkv;
+  const int64_t n_groups = cdiv(a.max_q, kRows) * a.num_seqs * (merged ? 1 : n_shards) * a.hkv;
   const int64_t blocks = cdiv(n_groups, 8) * 8 * (p.g / 2);
   if (blocks > INT32_MAX) return fail(CPA_ERR_INVALID_ARG, "partial attention: problem too large for one launch");
   p.n_groups = (int)n_groups;
@@ -608,7 +669,13 @@ cpa_status launch_attn_pp(const AttnArgs* shards, int n_shards, bool paged, hipS
   if (order_bytes > 0 && order_ws && order_ws_bytes >= order_bytes) {
     p.order = (const int*)order_ws;
     const int n_units = (int)(n_groups / a.hkv);
-    hipLaunchKernelGGL(pp_schedule_kernel, dim3(1), dim3(kSchedThreads), 0, st, p, n_units, (int*)order_ws);
+    hipLaunchKernelGGL(pp_schedule_kernel, dim3(1), dim3(kSchedThreads), 0, st, p, n_units, merged ? 1 : 0,
+                       (int*)order_ws);
+  }
+  if (merged) {
+    if (a.d == 64) merged->o_bf16 ? pp_launch<64, false, true, true>(p, nb, st) : pp_launch<64, false, false, true>(p, nb, st);
+    else merged->o_bf16 ? pp_launch<128, false, true, true>(p, nb, st) : pp_launch<128, false, false, true>(p, nb, st);
+    return check_launch("cpa_partial_attn_merged");
   }
   if (a.d == 64) {
     if (paged) a.o_bf16 ? pp_launch<64, true, true>(p, nb, st) : pp_launch<64, true, false>(p, nb, st);

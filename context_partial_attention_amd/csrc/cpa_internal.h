@@ -66,11 +66,19 @@ cpa_status launch_attn_mfma(const AttnArgs& a, bool paged, hipStream_t st);
 // each with its own output. With contiguous shards an optional order
 // workspace of attn_pp_order_bytes() lets a pre-pass run the heaviest tile
 // units first (0 bytes: the problem is too large to sort, index order).
+// With `merged`, one workgroup walks the visible keys of every shard in one
+// online softmax and writes only the merged (O, LSE) (the shards' own o, lse
+// are not used).
 constexpr int kMaxShards = 8;
+struct MergedOut {
+  void* o;
+  bool o_bf16;
+  float* lse;
+};
 bool attn_pp_supported(const AttnArgs& a);
 size_t attn_pp_order_bytes(int n_shards, int num_seqs, int max_q);
 cpa_status launch_attn_pp(const AttnArgs* shards, int n_shards, bool paged, hipStream_t st,
-                          void* order_ws = nullptr, size_t order_ws_bytes = 0);
+                          void* order_ws = nullptr, size_t order_ws_bytes = 0, const MergedOut* merged = nullptr);
 size_t decode_workspace_bytes(int32_t num_seqs, int32_t max_blocks, int32_t block_size, int32_t hq, int32_t d);
 cpa_status launch_attn_decode(const AttnArgs& a, hipStream_t st);
 

@@ -179,6 +179,16 @@ class Runner:
                                outs=self.o_parts, lses=self.lse_parts,
                                workspace=self.workspace if ordered else None, stream=stream)
 
+    def merged_walk(self, stream=None, out=None, lse=None):
+        """The merged pass-KV result in one walk over all resident shards
+        (writes self.o and self.lse unless other outputs are given)."""
+        inp, w = self.inp, self.w
+        st = inp["steps"]
+        cpa.partial_attn_merged(inp["q"], inp["q_pos"], inp["cu_q"], [s["k"] for s in st], [s["v"] for s in st],
+                                [s["k_pos"] for s in st], [s["cu_k"] for s in st], inp["max_q"], w.scale, True,
+                                out=self.o if out is None else out, lse=self.lse if lse is None else lse,
+                                workspace=self.workspace, stream=stream)
+
     def merge(self, stream=None):
         cpa.lse_merge(self.o_parts, self.lse_parts, out=self.o, lse_out=self.lse, stream=stream)
 

@@ -181,6 +181,33 @@ cpa_status cpa_partial_attn_multi(int32_t n_shards, const void* q, const int32_t
                                   void* workspace, size_t workspace_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------
+ * cpa_partial_attn_merged — the merged result of the pass-KV steps over
+ * n_shards resident contiguous KV shards, computed in one walk (device).
+ *
+ * [PASSKV], Purpose: a rank's queries attend to every KV shard in turn and
+ * the step partials are merged exactly. The merge of disjoint key sets is the
+ * softmax over their union, so one workgroup per query tile can walk the
+ * visible keys of all shards with a single online softmax and write the
+ * merged (O, LSE) directly: the same result as cpa_partial_attn_multi
+ * followed by cpa_lse_merge (up to rounding order), without the fp32
+ * partials or the separate merge pass.
+ *
+ * In: as cpa_partial_attn_multi (n_shards in [1, 8], host arrays of device
+ *   pointers k, v, k_pos, cu_k; workspace as there, optional).
+ * Out (device): o [Tq][hq][d] in o_dtype; lse [Tq][hq] float (natural log).
+ * Supported: in_dtype CPA_BF16 with an even GQA group (hq / hkv); anything
+ *   else is CPA_ERR_UNSUPPORTED (compute the partials and merge instead).
+ * Errors: as cpa_partial_attn_multi.
+ * ------------------------------------------------------------------------- */
+cpa_status cpa_partial_attn_merged(int32_t n_shards, const void* q, const int32_t* q_pos,
+                                   const int32_t* cu_q, const void* const* k, const void* const* v,
+                                   const int32_t* const* k_pos, const int32_t* const* cu_k,
+                                   int32_t num_seqs, int32_t max_q, int32_t hq, int32_t hkv,
+                                   int32_t d, cpa_dtype in_dtype, float scale, cpa_mask mask,
+                                   void* o, cpa_dtype o_dtype, float* lse, void* workspace,
+                                   size_t workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
  * cpa_partial_attn_paged_workspace — bytes of device workspace that
  * cpa_partial_attn_paged needs for these sizes (host, no GPU access).
  * Zero when no workspace is needed (max_q > 1).

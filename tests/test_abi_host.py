@@ -169,3 +169,20 @@ def test_multi_shard_call_validation_before_gpu(cpa):
     assert n.value >= 29 * 4 * 2 * 4 and n.value % 256 == 0  # one int per (query tile, sequence, shard)
     assert lib.cpa_partial_attn_multi_workspace(2, 4, 0, ctypes.byref(n)) == 0 and n.value == 0
     assert lib.cpa_partial_attn_multi_workspace(9, 4, 100, ctypes.byref(n)) == -1
+
+
+def test_merged_call_validation_before_gpu(cpa):
+    lib = cpa.load_library()
+    fake = ctypes.c_void_p(0x1000)  # never dereferenced: validation fails first
+    arr = (ctypes.c_void_p * 9)(*([0x1000] * 9))
+
+    def merged(n, k=arr, hkv=2, d=128, dt=0, odt=1):
+        return lib.cpa_partial_attn_merged(n, fake, fake, fake, k, arr, arr, arr, 1, 4, 8, hkv, d, dt, 0.1, 1, fake,
+                                           odt, fake, None, 0, None)
+
+    assert merged(0) == -1 and merged(9) == -1  # shard count out of range
+    assert merged(2, k=None) == -1  # NULL pointer array
+    assert merged(2, hkv=3) == -1  # hq not a multiple of hkv
+    assert merged(2, d=96) == -2  # unsupported head dim
+    assert merged(2, hkv=8) == -2  # GQA group of 1: no merged walk
+    assert merged(2, dt=1) == -2  # fp32 inputs: no merged walk

@@ -171,6 +171,67 @@ def test_multi_shard_launch_equals_separate_calls(cpa, wl, harness, name, change
         assert_close(f64(run.o_parts[s]), f64(run.lse_parts[s]), o_ref, l_ref, f"multi {name} shard {s}", **tol)
 
 
+MERGED = [
+    ("cp2_r0_ragged", dict(lengths=(300, 517, 1000), batch=3, len_range=(), cp=2, rank=0)),
+    ("cp4_r2_d64_g4", dict(lengths=(777, 64, 2), batch=3, len_range=(), cp=4, rank=2, hq=8, hkv=2, d=64)),
+    ("cp8_r3_tiny", dict(lengths=(3, 0, 17, 250, 1), batch=5, len_range=(), cp=8, rank=3)),
+]
+
+
+@pytest.mark.parametrize("name,changes", MERGED, ids=[m[0] for m in MERGED])
+def test_merged_walk_all_elements(cpa, wl, harness, name, changes):
+    """The one-walk merged result equals the oracle's merge of the step
+    partials (every element), and the GPU's partials + merge to rounding."""
+    w = wl.scaled(wl.WORKLOADS["qwen2.5_3b_cp2_rank0"], name=name, seed=500 + len(name), **changes)
+    _say(f"case merged {name}")
+    inp = harness.build(w, device="cuda")
+    run = harness.Runner(inp)
+    for out_dtype in (torch.float32, torch.bfloat16):
+        o = torch.full_like(run.o, float("nan"), dtype=out_dtype)
+        lse = torch.full_like(run.lse, float("nan"))
+        run.merged_walk(out=o, lse=lse)
+        torch.cuda.synchronize()
+        _, _, merged = expected_pass_kv(inp, None)
+        assert_close(f64(o), f64(lse), merged[0], merged[1], f"merged walk {name} {out_dtype}")
+    run.step()  # partials + separate merge
+    torch.cuda.synchronize()
+    o32 = torch.empty_like(run.o, dtype=torch.float32)
+    l32 = torch.empty_like(run.lse)
+    run.merged_walk(out=o32, lse=l32)
+    torch.cuda.synchronize()
+    assert_close(f64(o32), f64(l32), f64(run.o), f64(run.lse), f"merged walk vs partials + merge {name}")
+
+
+@pytest.mark.parametrize("name", ["qwen2.5_3b_cp2_rank0", "llama3_8b_128k_cp4_rank1"])
+def test_merged_walk_full_size_sampled(cpa, wl, harness, name):
+    w = wl.WORKLOADS[name]
+    _say(f"case merged full-size {name}")
+    inp = harness.build(w, device="cuda")
+    run = harness.Runner(inp)
+    run.merged_walk()
+    torch.cuda.synchronize()
+    assert not torch.isnan(run.o).any() and torch.isfinite(run.lse).all()
+    vmax = max(float(d[2].float().abs().max()) for d in inp["draws"])
+    assert float(run.o.float().abs().max()) <= vmax * (1 + 2 ** -8) + 1e-3
+    rows = sample_rows(inp["cu_q_host"], inp["q_positions_host"], n_random=48, seed=w.seed)
+    rows_, _, merged = expected_pass_kv(inp, rows)
+    ridx = torch.as_tensor(rows_, device="cuda")
+    e = assert_close(f64(run.o[ridx]), f64(run.lse[ridx]), merged[0], merged[1], f"{name} merged walk")
+    _say(f"  merged walk: max|dO|={e[0]:.2e} max|dLSE|={e[1]:.2e} over {len(rows_)} rows")
+
+
+def test_merged_walk_unsupported_cases(cpa, wl, harness):
+    """An odd GQA group or fp32 inputs are refused (compute partials + merge instead)."""
+    for name, changes in (("odd", dict(hq=3, hkv=1)), ("fp32", dict(dtype=torch.float32))):
+        w = wl.scaled(wl.WORKLOADS["qwen2.5_3b_cp2_rank0"], name=name, lengths=(100,), batch=1, len_range=(),
+                      **changes)
+        inp = harness.build(w, device="cuda")
+        run = harness.Runner(inp)
+        with pytest.raises(cpa.CpaError) as err:
+            run.merged_walk()
+        assert err.value.status == -2
+
+
 def test_invariants_ones_and_zero_keys(cpa, wl, harness):
     """V = 1 gives O = 1 on every row that sees a key; K = 0 gives
     LSE = ln(#visible keys) exactly enough to check the mask counts."""
