@@ -189,6 +189,21 @@ class Runner:
                                 out=self.o if out is None else out, lse=self.lse if lse is None else lse,
                                 workspace=self.workspace, stream=stream)
 
+    def capture(self, fn=None):
+        """Captures one call of `fn` (default: step) into a HIP graph and returns
+        it. Every kernel of the path is a plain launch on the current stream
+        (no memsets, no allocations), so replays repeat the eager results."""
+        fn = fn or self.step
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            fn()
+        torch.cuda.current_stream().wait_stream(side)
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            fn()
+        return graph
+
     def merge(self, stream=None):
         cpa.lse_merge(self.o_parts, self.lse_parts, out=self.o, lse_out=self.lse, stream=stream)
 

@@ -232,6 +232,43 @@ def test_merged_walk_unsupported_cases(cpa, wl, harness):
         assert err.value.status == -2
 
 
+GRAPH_CASES = [
+    ("pass_kv", "qwen2.5_3b_cp2_rank0", dict(lengths=(300, 517, 1000), batch=3, len_range=(), cp=2, rank=1)),
+    ("pass_q", "chunked_prefill_passq_cp4", dict(batch=2, cached=1000, new=300, cp=4, rank=0, interleave=8)),
+    ("decode", "allgather_decode_cp2", dict(batch=16, len_range=(1, 3000), lengths=(), cp=2, rank=0, interleave=8)),
+]
+
+
+@pytest.mark.parametrize("kind,base,changes", GRAPH_CASES, ids=[c[0] for c in GRAPH_CASES])
+def test_graph_replay_matches_eager(cpa, wl, harness, kind, base, changes):
+    """The step captured in a HIP graph: three replays, each after other eager
+    work on the same buffers, each bit-identical to the eager step."""
+    w = wl.scaled(wl.WORKLOADS[base], name=f"graph_{kind}", seed=700 + len(kind), kind=kind, **changes)
+    _say(f"case graph {kind}")
+    inp = harness.build(w, device="cuda")
+    run = harness.Runner(inp)
+    cases = [(run.step, lambda: [run.o, run.lse] + run.o_parts + run.lse_parts)]
+    if kind == "pass_kv":
+        cases.append((run.merged_walk, lambda: [run.o, run.lse]))
+    for fn, outputs in cases:
+        fn()
+        torch.cuda.synchronize()
+        ref = [t.clone() for t in outputs()]
+        graph = run.capture(fn)
+        for rep in range(3):
+            for t in outputs():
+                t.fill_(float("nan"))
+            torch.cuda.synchronize()
+            graph.replay()
+            torch.cuda.synchronize()
+            for i, (a, b) in enumerate(zip(outputs(), ref)):
+                assert torch.equal(a, b), f"{kind} {fn.__name__} replay {rep}: output {i} differs from eager"
+            # eager work on the same buffers between replays
+            run.partial(0)
+            run.merge()
+            torch.cuda.synchronize()
+
+
 def test_invariants_ones_and_zero_keys(cpa, wl, harness):
     """V = 1 gives O = 1 on every row that sees a key; K = 0 gives
     LSE = ln(#visible keys) exactly enough to check the mask counts."""
