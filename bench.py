@@ -349,7 +349,7 @@ def main():
                     "replayed as one captured HIP graph",
         },
         "roofline": {
-            "kernel": "attn_pp_kernel<128, contiguous, fp32 out>, both pass-KV steps in one launch "
+            "kernel": "attn_pp_kernel<128, contiguous, fp32 out, partials>, both pass-KV steps in one launch "
                       "(event time includes its launch-order pre-pass)",
             "bound": "mfma",
             "achieved": achieved,
