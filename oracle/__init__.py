@@ -17,4 +17,5 @@ from .cpattn_oracle import (  # noqa: F401
     partial_attn,
     lse_merge,
     visible_pairs,
+    choose_pass,
 )

@@ -302,3 +302,29 @@ def visible_pairs(q_pos, cu_q, k_pos, cu_k, causal: bool = True) -> int:
         for p in q_pos[cu_q[b]:cu_q[b + 1]]:
             total += int(np.count_nonzero(kp <= p)) if causal else len(kp)
     return total
+
+
+# ----------------------------------------------------------------------------
+# Choice of the exchanged shard (host policy)
+# ----------------------------------------------------------------------------
+
+
+def choose_pass(q_lens, kv_lens, hq: int, hkv: int, d: int, elem_bytes: int = 2) -> dict:
+    """Pass KV or pass Q for a prefill batch ([PASSKV], Purpose: the choice
+    follows the relative sizes of the Q and KV tensors; full prefill prefers
+    passing KV because a KV head usually serves more than two query heads,
+    chunked prefill with a cache much longer than the new tokens prefers
+    passing Q).
+
+    Reading: compare the bytes each scheme moves around the ring for the
+    batch, K plus V of every context token (2 * hkv * d per token) against Q
+    of every new token (hq * d per token); pass KV iff strictly fewer bytes.
+    For full prefill (kv_lens == q_lens) this is hq / hkv > 2, the pages'
+    statement. q_lens: new tokens per sequence; kv_lens: context tokens per
+    sequence (cached + new).
+    """
+    t_q = int(sum(int(x) for x in q_lens))
+    t_kv = int(sum(int(x) for x in kv_lens))
+    kv_bytes = 2 * hkv * d * elem_bytes * t_kv
+    q_bytes = hq * d * elem_bytes * t_q
+    return {"pass_kv": kv_bytes < q_bytes, "kv_bytes": kv_bytes, "q_bytes": q_bytes}

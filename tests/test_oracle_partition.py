@@ -152,3 +152,39 @@ def test_placement_packs_sequences():
         seg = pl["local_to_global"][pl["cu_local"][b]:pl["cu_local"][b + 1]]
         assert np.all(seg < L)
         assert np.all(np.diff(seg) > 0)
+
+
+# ----------------------------------------------------------------- choice of the exchanged shard
+
+
+def test_choose_pass_follows_the_pages_statements():
+    """[PASSKV], Purpose: full prefill passes KV when a KV head serves more than
+    two query heads; chunked prefill with a much longer cache passes Q."""
+    # full prefill, GQA groups of 8 (the Qwen2.5-3B and Llama-3-8B shapes): pass KV
+    assert oracle.choose_pass([4096, 2048], [4096, 2048], hq=16, hkv=2, d=128)["pass_kv"]
+    assert oracle.choose_pass([131072], [131072], hq=32, hkv=8, d=128)["pass_kv"]
+    # full prefill without grouping (MHA, one query head per KV head): pass Q
+    assert not oracle.choose_pass([4096], [4096], hq=32, hkv=32, d=128)["pass_kv"]
+    # chunked prefill, 4096 new tokens on a 65536-token cache, groups of 8: pass Q
+    assert not oracle.choose_pass([4096, 4096], [69632, 69632], hq=16, hkv=2, d=128)["pass_kv"]
+
+
+@pytest.mark.parametrize("g", [1, 2, 3, 4, 8])
+def test_choose_pass_full_prefill_boundary_is_group_of_two(g):
+    """With kv_lens == q_lens the rule reduces to hq / hkv > 2 (closed form),
+    whatever the lengths, head dim or element size."""
+    rng = np.random.default_rng(g)
+    lens = rng.integers(1, 5000, size=5)
+    for d, eb in ((64, 2), (128, 2), (128, 4)):
+        r = oracle.choose_pass(lens, lens, hq=4 * g, hkv=4, d=d, elem_bytes=eb)
+        assert r["pass_kv"] == (g > 2)
+        assert r["kv_bytes"] == 2 * 4 * d * eb * int(lens.sum())
+        assert r["q_bytes"] == 4 * g * d * eb * int(lens.sum())
+
+
+def test_choose_pass_crossover_in_cache_length():
+    """Chunked prefill: with q new tokens and group g, pass KV holds exactly while
+    the context is shorter than g*q/2 tokens (brute force over lengths)."""
+    for g, q in ((8, 100), (4, 37), (2, 64)):
+        for ctx in range(q, g * q):
+            assert oracle.choose_pass([q], [ctx], hq=2 * g, hkv=2, d=64)["pass_kv"] == (2 * ctx < g * q)
