@@ -13,6 +13,7 @@ from .binding import (  # noqa: F401
     MASK_CAUSAL,
     MASK_NONE,
     CpaError,
+    choose_pass,
     cp_partition,
     library_path,
     load_library,

@@ -54,6 +54,8 @@ def load_library():
     lib.cpa_cp_partition.argtypes = [_i32, _i32p, _i32, _i32, _i32p, _i32p, _i32p, _i32p, _i64, _i64p]
     lib.cpa_rr_placement.restype = _i32
     lib.cpa_rr_placement.argtypes = [_i32, _i32p, _i32, _i32, _i32, _i32p, _i32p, _i64, _i64p]
+    lib.cpa_choose_pass.restype = _i32
+    lib.cpa_choose_pass.argtypes = [_i32, _i32p, _i32p, _i32, _i32, _i32, _i32, _i32p, _i64p, _i64p]
     lib.cpa_partial_attn.restype = _i32
     lib.cpa_partial_attn.argtypes = [_p, _p, _p, _p, _p, _p, _p, _i32, _i32, _i32, _i32, _i32, _i32, _f32, _i32,
                                      _p, _i32, _p, _p]
@@ -130,6 +132,19 @@ def rr_placement(seq_lens, cp_size: int, rank: int, interleave: int) -> dict:
     cu = np.zeros(nseq + 1, dtype=np.int32)
     cu[1:] = np.cumsum(local)
     return {"local_lens": local, "cu_local": cu, "local_to_global": l2g}
+
+
+def choose_pass(q_lens, kv_lens, hq: int, hkv: int, d: int, elem_bytes: int = 2) -> dict:
+    """Pass KV or pass Q for a prefill batch: {"pass_kv", "kv_bytes", "q_bytes"}."""
+    lib = load_library()
+    ql, kl = _i32_array(q_lens), _i32_array(kv_lens)
+    if len(ql) != len(kl):
+        raise ValueError("q_lens and kv_lens need one entry per sequence")
+    pk = ctypes.c_int32(0)
+    kvb, qb = ctypes.c_int64(0), ctypes.c_int64(0)
+    _check("cpa_choose_pass", lib.cpa_choose_pass(len(ql), _ptr(ql), _ptr(kl), hq, hkv, d, elem_bytes,
+                                                  ctypes.byref(pk), ctypes.byref(kvb), ctypes.byref(qb)))
+    return {"pass_kv": bool(pk.value), "kv_bytes": kvb.value, "q_bytes": qb.value}
 
 
 # --------------------------------------------------------------- device calls

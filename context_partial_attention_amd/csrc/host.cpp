@@ -138,3 +138,29 @@ extern "C" cpa_status cpa_rr_placement(int32_t num_seqs, const int32_t* seq_lens
   }
   return CPA_OK;
 }
+
+// Exchanged-shard choice: bytes of K+V over the context against bytes of Q over
+// the new tokens; pass KV iff strictly fewer.
+extern "C" cpa_status cpa_choose_pass(int32_t num_seqs, const int32_t* q_lens, const int32_t* kv_lens, int32_t hq,
+                                      int32_t hkv, int32_t d, int32_t elem_bytes, int32_t* pass_kv, int64_t* kv_bytes,
+                                      int64_t* q_bytes) {
+  const char* fn = "cpa_choose_pass";
+  if (!pass_kv) return fail(CPA_ERR_INVALID_ARG, "%s: pass_kv is NULL", fn);
+  if (num_seqs < 0 || (num_seqs > 0 && (!q_lens || !kv_lens)))
+    return fail(CPA_ERR_INVALID_ARG, "%s: bad sequence arrays", fn);
+  if (hq < 1 || hkv < 1 || d < 1 || elem_bytes < 1) return fail(CPA_ERR_INVALID_ARG, "%s: sizes must be >= 1", fn);
+  __int128 t_q = 0, t_kv = 0;
+  for (int32_t b = 0; b < num_seqs; ++b) {
+    if (q_lens[b] < 0 || kv_lens[b] < 0) return fail(CPA_ERR_INVALID_ARG, "%s: negative length", fn);
+    t_q += q_lens[b];
+    t_kv += kv_lens[b];
+  }
+  const __int128 kvb = t_kv * 2 * hkv * d * elem_bytes;
+  const __int128 qb = t_q * hq * d * elem_bytes;
+  const __int128 lim = INT64_MAX;
+  if (kvb > lim || qb > lim) return fail(CPA_ERR_INVALID_ARG, "%s: byte totals overflow int64", fn);
+  *pass_kv = kvb < qb ? 1 : 0;
+  if (kv_bytes) *kv_bytes = (int64_t)kvb;
+  if (q_bytes) *q_bytes = (int64_t)qb;
+  return CPA_OK;
+}

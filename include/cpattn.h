@@ -116,6 +116,29 @@ cpa_status cpa_rr_placement(int32_t num_seqs, const int32_t* seq_lens, int32_t c
                             int32_t* local_to_global, int64_t cap, int64_t* n_out);
 
 /* ---------------------------------------------------------------------------
+ * cpa_choose_pass — pass KV or pass Q for a prefill batch (host).
+ *
+ * [PASSKV], Purpose: which shard to exchange follows the relative sizes of
+ * the Q and KV tensors; full prefill passes KV because a KV head usually
+ * serves more than two query heads, chunked prefill with a cache much longer
+ * than the new tokens passes Q. The rule here compares the bytes each scheme
+ * moves for the batch: K and V of every context token (2*hkv*d*elem_bytes
+ * each) against Q of every new token (hq*d*elem_bytes each); pass KV iff
+ * strictly fewer. With kv_lens == q_lens (full prefill) this is hq/hkv > 2.
+ *
+ * In:  num_seqs >= 0; q_lens[num_seqs] new tokens and kv_lens[num_seqs]
+ *      context tokens (cached + new) per sequence, all >= 0 (host);
+ *      hq, hkv, d, elem_bytes >= 1.
+ * Out: *pass_kv = 1 (pass KV) or 0 (pass Q), required; *kv_bytes, *q_bytes
+ *      the two totals (each may be NULL).
+ * Errors: CPA_ERR_INVALID_ARG on NULL arrays with num_seqs > 0, negative
+ *      lengths, sizes < 1, or totals above INT64_MAX.
+ * ------------------------------------------------------------------------- */
+cpa_status cpa_choose_pass(int32_t num_seqs, const int32_t* q_lens, const int32_t* kv_lens,
+                           int32_t hq, int32_t hkv, int32_t d, int32_t elem_bytes,
+                           int32_t* pass_kv, int64_t* kv_bytes, int64_t* q_bytes);
+
+/* ---------------------------------------------------------------------------
  * cpa_partial_attn — one pass-KV step: a packed Q shard against one packed,
  * contiguous KV shard, giving partial O and LSE (device).
  *

@@ -186,3 +186,32 @@ def test_merged_call_validation_before_gpu(cpa):
     assert merged(2, d=96) == -2  # unsupported head dim
     assert merged(2, hkv=8) == -2  # GQA group of 1: no merged walk
     assert merged(2, dt=1) == -2  # fp32 inputs: no merged walk
+
+
+def test_choose_pass_matches_oracle(cpa):
+    """Host choice of the exchanged shard: bit-exact against the oracle on
+    random batches, and the pages' two cases."""
+    import oracle
+
+    rng = np.random.default_rng(11)
+    for _ in range(200):
+        nb = int(rng.integers(0, 6))
+        q = rng.integers(0, 9000, size=nb)
+        kv = q + rng.integers(0, 70000, size=nb)
+        hkv = int(rng.choice([1, 2, 4, 8]))
+        hq = hkv * int(rng.integers(1, 9))
+        d, eb = int(rng.choice([64, 128])), int(rng.choice([1, 2, 4]))
+        assert cpa.choose_pass(q, kv, hq, hkv, d, eb) == oracle.choose_pass(q, kv, hq, hkv, d, eb)
+    assert cpa.choose_pass([6706], [6706], 16, 2, 128)["pass_kv"]  # full prefill, groups of 8
+    assert not cpa.choose_pass([4096, 4096], [69632, 69632], 16, 2, 128)["pass_kv"]  # chunked, long cache
+
+
+def test_choose_pass_errors(cpa):
+    lib = cpa.load_library()
+    pk = ctypes.c_int32(7)
+    lens = (ctypes.c_int32 * 2)(5, -1)
+    assert lib.cpa_choose_pass(2, lens, lens, 8, 2, 64, 2, ctypes.byref(pk), None, None) == -1  # negative length
+    assert lib.cpa_choose_pass(1, None, lens, 8, 2, 64, 2, ctypes.byref(pk), None, None) == -1  # NULL array
+    assert lib.cpa_choose_pass(1, lens, lens, 8, 0, 64, 2, ctypes.byref(pk), None, None) == -1  # hkv 0
+    assert lib.cpa_choose_pass(0, None, None, 8, 2, 64, 2, None, None, None) == -1  # NULL result
+    assert lib.cpa_choose_pass(0, None, None, 8, 2, 64, 2, ctypes.byref(pk), None, None) == 0 and pk.value == 0
