@@ -19,6 +19,7 @@ from .binding import (  # noqa: F401
     load_library,
     lse_merge,
     partial_attn,
+    partial_attn_accumulate,
     partial_attn_merged,
     partial_attn_multi,
     partial_attn_multi_workspace,

@@ -70,6 +70,9 @@ def load_library():
     lib.cpa_partial_attn_merged.argtypes = [_i32, _p, _p, _p, ctypes.POINTER(_p), ctypes.POINTER(_p),
                                             ctypes.POINTER(_p), ctypes.POINTER(_p), _i32, _i32, _i32, _i32, _i32,
                                             _i32, _f32, _i32, _p, _i32, _p, _p, ctypes.c_size_t, _p]
+    lib.cpa_partial_attn_accumulate.restype = _i32
+    lib.cpa_partial_attn_accumulate.argtypes = [_p, _p, _p, _p, _p, _p, _p, _i32, _i32, _i32, _i32, _i32, _i32, _f32,
+                                                _i32, _p, _p, _p, _i32, _p]
     lib.cpa_partial_attn_paged_workspace.restype = _i32
     lib.cpa_partial_attn_paged_workspace.argtypes = [_i32, _i32, _i32, _i32, _i32, _i32,
                                                      ctypes.POINTER(ctypes.c_size_t)]
@@ -261,6 +264,21 @@ def partial_attn_merged(q, q_pos, cu_q, ks, vs, k_poss, cu_ks, max_q: int, scale
         _dev(workspace, "workspace"), 0 if workspace is None else workspace.numel() * workspace.element_size(),
         _stream(stream)))
     return out, lse
+
+
+def partial_attn_accumulate(q, q_pos, cu_q, k, v, k_pos, cu_k, max_q: int, scale: float, o_acc, lse_acc,
+                            causal: bool = True, out=None, stream=None):
+    """One pass-KV step folded into the running (o_acc, lse_acc) (fp32, in place); `out`, if given,
+    also receives the merged O (bf16 or fp32). Returns (o_acc, lse_acc)."""
+    tq, hq, d = q.shape
+    hkv = k.shape[1]
+    num_seqs = cu_q.numel() - 1
+    _check("cpa_partial_attn_accumulate", load_library().cpa_partial_attn_accumulate(
+        _dev(q, "q"), _dev(q_pos, "q_pos"), _dev(cu_q, "cu_q"), _dev(k, "k"), _dev(v, "v"), _dev(k_pos, "k_pos"),
+        _dev(cu_k, "cu_k"), num_seqs, int(max_q), hq, hkv, d, _dtype_code(q), float(scale),
+        MASK_CAUSAL if causal else MASK_NONE, _dev(o_acc, "o_acc"), _dev(lse_acc, "lse_acc"), _dev(out, "out"),
+        F32 if out is None else _dtype_code(out), _stream(stream)))
+    return o_acc, lse_acc
 
 
 def partial_attn_paged_workspace(num_seqs: int, max_q: int, max_blocks: int, block_size: int, hq: int,

@@ -186,6 +186,48 @@ extern "C" cpa_status cpa_partial_attn_merged(int32_t n_shards, const void* q, c
   return launch_attn_pp(args, n_shards, /*paged=*/false, (hipStream_t)stream, workspace, workspace_bytes, &out);
 }
 
+extern "C" cpa_status cpa_partial_attn_accumulate(const void* q, const int32_t* q_pos, const int32_t* cu_q,
+                                                  const void* k, const void* v, const int32_t* k_pos,
+                                                  const int32_t* cu_k, int32_t num_seqs, int32_t max_q, int32_t hq,
+                                                  int32_t hkv, int32_t d, cpa_dtype in_dtype, float scale,
+                                                  cpa_mask mask, float* o_acc, float* lse_acc, void* o_out,
+                                                  cpa_dtype o_out_dtype, void* stream) {
+  const char* fn = "cpa_partial_attn_accumulate";
+  if (in_dtype != CPA_BF16 && in_dtype != CPA_F32) return fail(CPA_ERR_INVALID_ARG, "%s: bad in_dtype", fn);
+  if (o_out_dtype != CPA_BF16 && o_out_dtype != CPA_F32) return fail(CPA_ERR_INVALID_ARG, "%s: bad o_out_dtype", fn);
+  cpa_status st = check_common(fn, q, q_pos, cu_q, k, v, num_seqs, max_q, hq, hkv, d, scale, mask, o_acc, lse_acc);
+  if (st != CPA_OK) return st;
+  if (num_seqs > 0 && max_q > 0) {
+    if (!cu_k) return fail(CPA_ERR_INVALID_ARG, "%s: cu_k is NULL", fn);
+    if (mask == CPA_MASK_CAUSAL && !k_pos) return fail(CPA_ERR_INVALID_ARG, "%s: k_pos is NULL", fn);
+  }
+  AttnArgs a{};
+  a.q = q;
+  a.q_pos = q_pos;
+  a.cu_q = cu_q;
+  a.k = k;
+  a.v = v;
+  a.k_pos = mask == CPA_MASK_CAUSAL ? k_pos : nullptr;
+  a.cu_k = cu_k;
+  a.num_seqs = num_seqs;
+  a.max_q = max_q;
+  a.hq = hq;
+  a.hkv = hkv;
+  a.d = d;
+  a.scale = scale;
+  a.causal = mask == CPA_MASK_CAUSAL;
+  a.o = o_out;
+  a.o_bf16 = o_out_dtype == CPA_BF16;
+  a.lse = lse_acc;
+  if (in_dtype != CPA_BF16 || !attn_pp_supported(a))
+    return fail(CPA_ERR_UNSUPPORTED, "%s: needs bf16 inputs and an even GQA group (hq / hkv)", fn);
+  st = check_device();
+  if (st != CPA_OK) return st;
+  if (num_seqs == 0 || max_q == 0) return CPA_OK;
+  const AccumIO io{o_acc, lse_acc, o_out};
+  return launch_attn_pp(&a, 1, /*paged=*/false, (hipStream_t)stream, nullptr, 0, nullptr, &io);
+}
+
 extern "C" cpa_status cpa_partial_attn_paged_workspace(int32_t num_seqs, int32_t max_q, int32_t max_blocks,
                                                        int32_t block_size, int32_t hq, int32_t d, size_t* bytes) {
   const char* fn = "cpa_partial_attn_paged_workspace";

@@ -81,6 +81,11 @@ struct PPParams {
   // Optional launch order (contiguous shards): order[i] is the tile unit
   // (group / hkv) the i-th unit slot runs; NULL runs units in index order.
   const int* order;
+  // Running merge (one contiguous shard): when o_acc is set, the partial is
+  // folded into (o_acc, lse_acc) in place, and o[0] (may be NULL) receives a
+  // copy of the merged O in the output dtype.
+  float* o_acc;
+  float* lse_acc;
 };
 
 // Column (LDS slot) of key `key` in a transposed V tile: within every 16
@@ -506,6 +511,49 @@ __global__ __launch_bounds__(kThreads, 1) void attn_pp_kernel(PPParams p) {
   if (!row_ok) return;
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
   const int64_t obase = ((int64_t)my_row * p.hq + h) * D;
+  if constexpr (!PAGED && !MERGED) {
+    if (p.o_acc) {
+      // exact merge of (o_acc, lse_acc) with this partial, in base 2: weights
+      // 2^(lse_s - lse) with lse = M + log2(sum_s 2^(lse_s - M)); an empty side
+      // (LSE -inf) has weight 0 and its O is not read into the sum
+      const int64_t li = (int64_t)my_row * p.hq + h;
+      const float lse_new = l_tot > 0.f ? m_run + hw_log2(l_tot) : kNegInf;
+      const float lse_old = p.lse_acc[li] * kLog2e;
+      const float mx = fmaxf(lse_old, lse_new);
+      float w_old = 0.f, c_new = 0.f, lse_m = kNegInf;
+      if (mx != kNegInf) {
+        const float e_old = hw_exp2(lse_old - mx), e_new = hw_exp2(lse_new - mx);
+        const float sum = e_old + e_new;
+        lse_m = mx + hw_log2(sum);
+        w_old = e_old / sum;
+        c_new = (e_new / sum) * inv;
+      }
+      const bool use_old = lse_old != kNegInf;
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db) {
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const int d0 = 32 * db + 8 * q4 + 4 * lc;
+          float* acc_p = p.o_acc + obase + d0;
+          const f32x4 old = use_old ? *(const f32x4*)acc_p : f32x4{};
+          f32x4 val;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) val[e] = fmaf(w_old, old[e], c_new * oacc[db][4 * q4 + e]);
+          *(f32x4*)acc_p = val;
+          if (p.o[0]) {
+            if constexpr (OUT_BF16) {
+              const u32x2 w = {pack_bf16x2(val[0], val[1]), pack_bf16x2(val[2], val[3])};
+              *(u32x2*)((uint16_t*)p.o[0] + obase + d0) = w;
+            } else {
+              *(f32x4*)((float*)p.o[0] + obase + d0) = val;
+            }
+          }
+        }
+      }
+      if (lc == 0) p.lse_acc[li] = lse_m * kLn2;
+      return;
+    }
+  }
 #pragma unroll
   for (int db = 0; db < D / 32; ++db) {
 #pragma unroll
@@ -626,8 +674,10 @@ size_t attn_pp_order_bytes(int n_shards, int num_seqs, int max_q) {
 }
 
 cpa_status launch_attn_pp(const AttnArgs* shards, int n_shards, bool paged, hipStream_t st, void* order_ws,
-                          size_t order_ws_bytes, const MergedOut* merged) {
+                          size_t order_ws_bytes, const MergedOut* merged, const AccumIO* accum) {
   if (merged && paged) return fail(CPA_ERR_INVALID_ARG, "partial attention: a merged walk needs contiguous shards");
+  if (accum && (paged || merged || n_shards != 1))
+    return fail(CPA_ERR_INVALID_ARG, "partial attention: a running merge takes one contiguous shard");
   if (n_shards < 1 || n_shards > kMaxShards) return fail(CPA_ERR_INVALID_ARG, "partial attention: bad shard count");
   const AttnArgs& a = shards[0];
   PPParams p{};
@@ -646,6 +696,12 @@ cpa_status launch_attn_pp(const AttnArgs* shards, int n_shards, bool paged, hipS
   if (merged) {  // one output: the exact merge over all shards
     p.o[0] = merged->o;
     p.lse[0] = merged->lse;
+  }
+  if (accum) {  // fold into the running (O, LSE); o[0] is the optional merged copy
+    p.o_acc = accum->o_acc;
+    p.lse_acc = accum->lse_acc;
+    p.o[0] = accum->o_out;
+    p.lse[0] = nullptr;
   }
   p.block_table = a.block_table;
   p.max_blocks = a.max_blocks;
@@ -684,7 +740,8 @@ cpa_status launch_attn_pp(const AttnArgs* shards, int n_shards, bool paged, hipS
     if (paged) a.o_bf16 ? pp_launch<128, true, true>(p, nb, st) : pp_launch<128, true, false>(p, nb, st);
     else a.o_bf16 ? pp_launch<128, false, true>(p, nb, st) : pp_launch<128, false, false>(p, nb, st);
   }
-  return check_launch(paged ? "cpa_partial_attn_paged (prefill)" : "cpa_partial_attn (bf16)");
+  return check_launch(paged ? "cpa_partial_attn_paged (prefill)"
+                             : (accum ? "cpa_partial_attn_accumulate" : "cpa_partial_attn (bf16)"));
 }
 
 }  // namespace cpa

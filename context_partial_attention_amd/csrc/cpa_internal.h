@@ -77,8 +77,17 @@ struct MergedOut {
 };
 bool attn_pp_supported(const AttnArgs& a);
 size_t attn_pp_order_bytes(int n_shards, int num_seqs, int max_q);
+// With `accum` (one contiguous shard), the partial is folded into the running
+// (o_acc, lse_acc) in place; o_out (may be NULL) gets a copy of the merged O in
+// the shard's output dtype.
+struct AccumIO {
+  float* o_acc;
+  float* lse_acc;
+  void* o_out;
+};
 cpa_status launch_attn_pp(const AttnArgs* shards, int n_shards, bool paged, hipStream_t st,
-                          void* order_ws = nullptr, size_t order_ws_bytes = 0, const MergedOut* merged = nullptr);
+                          void* order_ws = nullptr, size_t order_ws_bytes = 0, const MergedOut* merged = nullptr,
+                          const AccumIO* accum = nullptr);
 size_t decode_workspace_bytes(int32_t num_seqs, int32_t max_blocks, int32_t block_size, int32_t hq, int32_t d);
 cpa_status launch_attn_decode(const AttnArgs& a, hipStream_t st);
 

@@ -189,6 +189,20 @@ class Runner:
                                 out=self.o if out is None else out, lse=self.lse if lse is None else lse,
                                 workspace=self.workspace, stream=stream)
 
+    def ring_accumulate(self, stream=None, out=None):
+        """The pass-KV steps as a ring would run them: one shard at a time, each
+        folded into the running (o_parts[0], lse_parts[0]) (fp32); `out` (or
+        self.o) receives the merged O at the last step, self.lse the LSE."""
+        inp, w = self.inp, self.w
+        o_acc, lse_acc = self.o_parts[0], self.lse_parts[0]
+        lse_acc.fill_(float("-inf"))
+        for i, st in enumerate(inp["steps"]):
+            last = i == len(inp["steps"]) - 1
+            cpa.partial_attn_accumulate(inp["q"], inp["q_pos"], inp["cu_q"], st["k"], st["v"], st["k_pos"],
+                                        st["cu_k"], inp["max_q"], w.scale, o_acc, lse_acc,
+                                        out=(self.o if out is None else out) if last else None, stream=stream)
+        self.lse.copy_(lse_acc)
+
     def capture(self, fn=None):
         """Captures one call of `fn` (default: step) into a HIP graph and returns
         it. Every kernel of the path is a plain launch on the current stream

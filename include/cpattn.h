@@ -231,6 +231,33 @@ cpa_status cpa_partial_attn_merged(int32_t n_shards, const void* q, const int32_
                                    size_t workspace_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------
+ * cpa_partial_attn_accumulate — one pass-KV step folded into a running merge
+ * (device).
+ *
+ * [PASSKV], Purpose: in the pass-KV exchange a rank computes one partial per
+ * arriving KV shard and the partials are merged exactly. This call computes
+ * the partial of one contiguous KV shard (as cpa_partial_attn) and merges it
+ * in its epilogue with the running (o_acc, lse_acc) of the earlier steps, in
+ * place, by the rule of cpa_lse_merge; no partial is written.
+ *
+ * In: q ... mask as cpa_partial_attn (one shard). o_acc [Tq][hq][d] float and
+ *   lse_acc [Tq][hq] float (device, read and written): the merge of the
+ *   earlier steps; a row with lse_acc = -inf counts as empty and its o_acc is
+ *   not read (start a ring with lse_acc = -inf, or with a cpa_partial_attn
+ *   result in fp32). o_out (device, may be NULL) also receives the merged O
+ *   in o_out_dtype (for the last step, say).
+ * Supported: in_dtype CPA_BF16 with an even GQA group; anything else is
+ *   CPA_ERR_UNSUPPORTED.
+ * Errors: as cpa_partial_attn; CPA_ERR_INVALID_ARG for NULL o_acc / lse_acc.
+ * ------------------------------------------------------------------------- */
+cpa_status cpa_partial_attn_accumulate(const void* q, const int32_t* q_pos, const int32_t* cu_q,
+                                       const void* k, const void* v, const int32_t* k_pos,
+                                       const int32_t* cu_k, int32_t num_seqs, int32_t max_q,
+                                       int32_t hq, int32_t hkv, int32_t d, cpa_dtype in_dtype,
+                                       float scale, cpa_mask mask, float* o_acc, float* lse_acc,
+                                       void* o_out, cpa_dtype o_out_dtype, void* stream);
+
+/* ---------------------------------------------------------------------------
  * cpa_partial_attn_paged_workspace — bytes of device workspace that
  * cpa_partial_attn_paged needs for these sizes (host, no GPU access).
  * Zero when no workspace is needed (max_q > 1).

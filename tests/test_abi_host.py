@@ -215,3 +215,17 @@ def test_choose_pass_errors(cpa):
     assert lib.cpa_choose_pass(1, lens, lens, 8, 0, 64, 2, ctypes.byref(pk), None, None) == -1  # hkv 0
     assert lib.cpa_choose_pass(0, None, None, 8, 2, 64, 2, None, None, None) == -1  # NULL result
     assert lib.cpa_choose_pass(0, None, None, 8, 2, 64, 2, ctypes.byref(pk), None, None) == 0 and pk.value == 0
+
+
+def test_accumulate_call_validation_before_gpu(cpa):
+    lib = cpa.load_library()
+    fake = ctypes.c_void_p(0x1000)  # never dereferenced: validation fails first
+
+    def acc(o_acc=fake, lse_acc=fake, hkv=2, dt=0):
+        return lib.cpa_partial_attn_accumulate(fake, fake, fake, fake, fake, fake, fake, 1, 4, 8, hkv, 128, dt, 0.1,
+                                               1, o_acc, lse_acc, None, 0, None)
+
+    assert acc(o_acc=None) == -1 and acc(lse_acc=None) == -1  # NULL accumulator
+    assert acc(hkv=3) == -1  # hq not a multiple of hkv
+    assert acc(hkv=8) == -2  # GQA group of 1: not supported
+    assert acc(dt=1) == -2  # fp32 inputs: not supported

@@ -232,6 +232,32 @@ def test_merged_walk_unsupported_cases(cpa, wl, harness):
         assert err.value.status == -2
 
 
+@pytest.mark.parametrize("name,changes", MERGED, ids=[m[0] for m in MERGED])
+def test_ring_accumulate_all_elements(cpa, wl, harness, name, changes):
+    """Running merge: the shards folded in one at a time into (O, LSE) equal
+    the oracle's merged result; an accumulator row with LSE -inf is never
+    read (it holds NaN here); starting from a plain partial gives the same."""
+    w = wl.scaled(wl.WORKLOADS["qwen2.5_3b_cp2_rank0"], name=name, seed=600 + len(name), **changes)
+    _say(f"case ring {name}")
+    inp = harness.build(w, device="cuda")
+    run = harness.Runner(inp)
+    _, _, merged = expected_pass_kv(inp, None)
+    run.o_parts[0].fill_(float("nan"))
+    run.ring_accumulate()
+    torch.cuda.synchronize()
+    assert_close(f64(run.o), f64(run.lse), merged[0], merged[1], f"ring {name} (bf16 out)")
+    assert_close(f64(run.o_parts[0]), f64(run.lse_parts[0]), merged[0], merged[1], f"ring {name} (fp32 acc)")
+    # first step as a plain partial into the accumulator, the rest folded in
+    st = inp["steps"]
+    o_acc, lse_acc = cpa.partial_attn(inp["q"], inp["q_pos"], inp["cu_q"], st[0]["k"], st[0]["v"], st[0]["k_pos"],
+                                      st[0]["cu_k"], inp["max_q"], w.scale, True)
+    for s in st[1:]:
+        cpa.partial_attn_accumulate(inp["q"], inp["q_pos"], inp["cu_q"], s["k"], s["v"], s["k_pos"], s["cu_k"],
+                                    inp["max_q"], w.scale, o_acc, lse_acc)
+    torch.cuda.synchronize()
+    assert_close(f64(o_acc), f64(lse_acc), merged[0], merged[1], f"ring {name} from a partial")
+
+
 GRAPH_CASES = [
     ("pass_kv", "qwen2.5_3b_cp2_rank0", dict(lengths=(300, 517, 1000), batch=3, len_range=(), cp=2, rank=1)),
     ("pass_q", "chunked_prefill_passq_cp4", dict(batch=2, cached=1000, new=300, cp=4, rank=0, interleave=8)),
