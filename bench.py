@@ -191,6 +191,11 @@ def bench_workload(name: str, steps: int, warmup: int) -> dict:
             res["fused_walk_ms"] = fw_ms
             res["fused_walk_TFLOPs"] = sum(flops) / (fw_ms * 1e-3) / 1e12
             res["fused_walk_pct_bf16_peak"] = 100 * res["fused_walk_TFLOPs"] / PEAK_BF16_TFLOPS
+            # the same shards one at a time, each folded into a running (O, LSE)
+            # as a ring exchange would deliver them (cpa_partial_attn_accumulate)
+            ra_ms = per_launch_ms(run.ring_accumulate)
+            res["ring_accumulate_ms"] = ra_ms
+            res["ring_accumulate_TFLOPs"] = sum(flops) / (ra_ms * 1e-3) / 1e12
     del run, inp
     torch.cuda.empty_cache()
     return res
@@ -367,6 +372,8 @@ def main():
             "ms": h.get("fused_walk_ms"),
             "TFLOPs": h.get("fused_walk_TFLOPs"),
             "pct_bf16_peak": h.get("fused_walk_pct_bf16_peak"),
+            "ring_accumulate_ms": h.get("ring_accumulate_ms"),
+            "ring_accumulate_TFLOPs": h.get("ring_accumulate_TFLOPs"),
         },
     }
     if not args.no_cpu_baseline:
