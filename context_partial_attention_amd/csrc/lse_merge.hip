@@ -6,9 +6,10 @@
 // Purpose).
 //
 // HBM-bound: every byte of every partial is read once and the result written
-// once. One thread owns 4 consecutive elements of a row, issues all of its
-// n_parts loads before any arithmetic, and the LSE arithmetic is done in
-// base 2 on v_exp_f32 / v_log_f32.
+// once. One thread owns 8 consecutive elements of a row, issues all of its
+// loads before any arithmetic, and the LSE arithmetic is done in base 2 on
+// v_exp_f32 / v_log_f32. Two and four parts (the common CP sizes) have their
+// own instantiations so the registers are sized for them.
 #include "cpa_internal.h"
 #include "device_common.h"
 
@@ -21,63 +22,87 @@ struct MergeParts {
   const float* lse[kMaxParts];
 };
 
-template <int D, bool PART_BF16, bool OUT_BF16>
+// NP > 0: exactly NP parts (compile time, registers sized for them); NP == 0:
+// n_parts at run time, up to kMaxParts. Each thread owns two groups of 4
+// elements of a row, half a row apart, so that every part adds two loads to
+// the thread's loads in flight while each load instruction of a wave still
+// reads one contiguous span.
+template <int D, int NP, bool PART_BF16, bool OUT_BF16>
 __global__ __launch_bounds__(256) void lse_merge_kernel(MergeParts parts, int n_parts, int64_t rows,
                                                         void* __restrict__ o_out, float* __restrict__ lse_out) {
-  constexpr int kThreadsPerRow = D / 4;
+  constexpr int kThreadsPerRow = D / 8;
   constexpr int kRowsPerBlock = 256 / kThreadsPerRow;
+  constexpr int kP = NP > 0 ? NP : kMaxParts;
   const int64_t row = (int64_t)blockIdx.x * kRowsPerBlock + threadIdx.x / kThreadsPerRow;
   const int c = threadIdx.x % kThreadsPerRow;
   if (row >= rows) return;
-  const int64_t elem = row * D + c * 4;
+  const int np = NP > 0 ? NP : n_parts;
+  const int64_t elem = row * D + c * 4;  // and elem + D / 2
 
-  float l2[kMaxParts];
-  f32x4 x[kMaxParts];
+  float l2[kP];
+  f32x4 xa[kP], xb[kP];
 #pragma unroll
-  for (int s = 0; s < kMaxParts; ++s) {
-    if (s < n_parts) {
+  for (int s = 0; s < kP; ++s) {
+    if (s < np) {
       l2[s] = parts.lse[s][row] * kLog2e;
       if constexpr (PART_BF16) {
-        const u32x2 w = __builtin_nontemporal_load((const u32x2*)((const uint16_t*)parts.o[s] + elem));
-        x[s] = f32x4{bf16_lo(w[0]), bf16_hi(w[0]), bf16_lo(w[1]), bf16_hi(w[1])};
+        const u32x2 wa = __builtin_nontemporal_load((const u32x2*)((const uint16_t*)parts.o[s] + elem));
+        const u32x2 wb = __builtin_nontemporal_load((const u32x2*)((const uint16_t*)parts.o[s] + elem + D / 2));
+        xa[s] = f32x4{bf16_lo(wa[0]), bf16_hi(wa[0]), bf16_lo(wa[1]), bf16_hi(wa[1])};
+        xb[s] = f32x4{bf16_lo(wb[0]), bf16_hi(wb[0]), bf16_lo(wb[1]), bf16_hi(wb[1])};
       } else {
-        x[s] = __builtin_nontemporal_load((const f32x4*)((const float*)parts.o[s] + elem));
+        xa[s] = __builtin_nontemporal_load((const f32x4*)((const float*)parts.o[s] + elem));
+        xb[s] = __builtin_nontemporal_load((const f32x4*)((const float*)parts.o[s] + elem + D / 2));
       }
     }
   }
   float m = kNegInf;
 #pragma unroll
-  for (int s = 0; s < kMaxParts; ++s)
-    if (s < n_parts) m = fmaxf(m, l2[s]);
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  for (int s = 0; s < kP; ++s)
+    if (s < np) m = fmaxf(m, l2[s]);
+  f32x4 acc_a = {0.f, 0.f, 0.f, 0.f}, acc_b = {0.f, 0.f, 0.f, 0.f};
   float lse2 = kNegInf;
   if (m != kNegInf) {
     float sum = 0.f;
 #pragma unroll
-    for (int s = 0; s < kMaxParts; ++s)
-      if (s < n_parts) sum += hw_exp2(l2[s] - m);
+    for (int s = 0; s < kP; ++s)
+      if (s < np) sum += hw_exp2(l2[s] - m);
     lse2 = m + hw_log2(sum);
 #pragma unroll
-    for (int s = 0; s < kMaxParts; ++s)
-      if (s < n_parts) {
+    for (int s = 0; s < kP; ++s)
+      if (s < np) {
         const float w = hw_exp2(l2[s] - lse2);  // 0 for an empty (-inf) part
-        acc += w * x[s];
+        acc_a += w * xa[s];
+        acc_b += w * xb[s];
       }
   }
   if constexpr (OUT_BF16) {
-    u32x2 w = {pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3])};
-    __builtin_nontemporal_store(w, (u32x2*)((uint16_t*)o_out + elem));
+    const u32x2 wa = {pack_bf16x2(acc_a[0], acc_a[1]), pack_bf16x2(acc_a[2], acc_a[3])};
+    const u32x2 wb = {pack_bf16x2(acc_b[0], acc_b[1]), pack_bf16x2(acc_b[2], acc_b[3])};
+    __builtin_nontemporal_store(wa, (u32x2*)((uint16_t*)o_out + elem));
+    __builtin_nontemporal_store(wb, (u32x2*)((uint16_t*)o_out + elem + D / 2));
   } else {
-    __builtin_nontemporal_store(acc, (f32x4*)((float*)o_out + elem));
+    __builtin_nontemporal_store(acc_a, (f32x4*)((float*)o_out + elem));
+    __builtin_nontemporal_store(acc_b, (f32x4*)((float*)o_out + elem + D / 2));
   }
   if (c == 0 && lse_out) lse_out[row] = lse2 * kLn2;
 }
 
+template <int D, int NP, bool PB, bool OB>
+static void launch_merge_np(const MergeParts& p, int n, int64_t rows, void* o, float* lse, hipStream_t st) {
+  constexpr int kRowsPerBlock = 256 / (D / 8);
+  const int64_t blocks = cdiv(rows, kRowsPerBlock);
+  hipLaunchKernelGGL((lse_merge_kernel<D, NP, PB, OB>), dim3((uint32_t)blocks), dim3(256), 0, st, p, n, rows, o,
+                     lse);
+}
+
 template <int D, bool PB, bool OB>
 static void launch_merge(const MergeParts& p, int n, int64_t rows, void* o, float* lse, hipStream_t st) {
-  constexpr int kRowsPerBlock = 256 / (D / 4);
-  const int64_t blocks = cdiv(rows, kRowsPerBlock);
-  hipLaunchKernelGGL((lse_merge_kernel<D, PB, OB>), dim3((uint32_t)blocks), dim3(256), 0, st, p, n, rows, o, lse);
+  switch (n) {
+    case 2: launch_merge_np<D, 2, PB, OB>(p, n, rows, o, lse, st); break;
+    case 4: launch_merge_np<D, 4, PB, OB>(p, n, rows, o, lse, st); break;
+    default: launch_merge_np<D, 0, PB, OB>(p, n, rows, o, lse, st); break;
+  }
 }
 
 }  // namespace cpa
@@ -102,7 +127,7 @@ extern "C" cpa_status cpa_lse_merge(int32_t n_parts, const void* const* o_parts,
     p.o[s] = o_parts[s];
     p.lse[s] = lse_parts[s];
   }
-  if (rows > (int64_t)INT32_MAX * 64) return fail(CPA_ERR_INVALID_ARG, "cpa_lse_merge: rows too large");
+  if (rows > (int64_t)INT32_MAX * 16) return fail(CPA_ERR_INVALID_ARG, "cpa_lse_merge: rows too large");
   cpa_status st = check_device();
   if (st != CPA_OK) return st;
   if (rows == 0) return CPA_OK;
