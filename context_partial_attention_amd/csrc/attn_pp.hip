@@ -39,6 +39,7 @@ namespace {
 constexpr int kBN = 64;        // keys per tile
 constexpr int kRows = 128;     // query rows per workgroup (per head)
 constexpr int kThreads = 512;  // 8 waves
+constexpr int kTabCap = 2048;  // paged: block-table entries of a workgroup staged in LDS (8 KiB)
 
 template <int D>
 struct PPTile {
@@ -187,9 +188,22 @@ __global__ __launch_bounds__(kThreads, 1) void attn_pp_kernel(PPParams p) {
     }
   };
   int seg0_ka = 0, seg0_end = 0, n = 0;  // n: tiles of the walk
+  // paged: the block-table entries the workgroup's visible keys use, staged
+  // in LDS once, so a tile's loads do not wait on a global table read
+  __shared__ int tab_sh[PAGED ? kTabCap : 1];
+  bool tab_in_lds = false;
   if constexpr (!MERGED) {
     seg_range(shard, seg0_ka, seg0_end);
     n = seg0_end > seg0_ka ? (seg0_end - seg0_ka + kBN - 1) / kBN : 0;
+    if constexpr (PAGED) {
+      const int nb = (seg0_end + 15) >> 4;  // <= max_blocks (seg0_end is clamped to it)
+      tab_in_lds = nb <= kTabCap;
+      if (tab_in_lds) {
+        const int* src = p.block_table + (int64_t)seq * p.max_blocks;
+        for (int b = tid; b < nb; b += kThreads) tab_sh[b] = src[b];
+        __syncthreads();
+      }
+    }
   } else {
     for (int sg = 0; sg < p.n_shards; ++sg) {
       int ka, ke;
@@ -255,15 +269,16 @@ __global__ __launch_bounds__(kThreads, 1) void attn_pp_kernel(PPParams p) {
     if constexpr (PAGED) {
       const int64_t slab = (int64_t)p.hkv * 16 * D;
       const int* tab = p.block_table + (int64_t)seq * p.max_blocks;
+      auto tab_at = [&](int b) { return tab_in_lds ? tab_sh[b] : tab[b]; };
 #pragma unroll
       for (int i = 0; i < T::kChunks; ++i) {
         const int r = r_first + i * T::kRowsPerPass;
         if (!last) {
-          const int blk = tab[__builtin_amdgcn_readfirstlane((j0 + r) >> 4)];
+          const int blk = __builtin_amdgcn_readfirstlane(tab_at(__builtin_amdgcn_readfirstlane((j0 + r) >> 4)));
           regs[i] = *(const u32x4*)(src + (int64_t)blk * slab + (int64_t)kvh * 16 * D + off[i]);
         } else {
           const int j = min(j0 + r, n_end - 1);
-          const int blk = tab[j >> 4];
+          const int blk = tab_at(j >> 4);
           regs[i] = *(const u32x4*)(src + (int64_t)blk * slab + ((int64_t)kvh * 16 + (j & 15)) * D + c8 * 8);
         }
       }
@@ -287,7 +302,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_pp_kernel(PPParams p) {
     for (int r = 0; r < 2; ++r) {
       const int j = min(j0 + 2 * v_kp + r, n_end - 1);
       if constexpr (PAGED) {
-        const int blk = p.block_table[(int64_t)seq * p.max_blocks + (j >> 4)];
+        const int blk = tab_in_lds ? tab_sh[j >> 4] : p.block_table[(int64_t)seq * p.max_blocks + (j >> 4)];
         regs[r] = *(const u32x4*)(vmat + ((int64_t)blk * p.hkv + kvh) * 16 * D + (j & 15) * D + v_dc * 8);
       } else {
         regs[r] = *(const u32x4*)(vmat + ((int64_t)j * p.hkv + kvh) * D + v_dc * 8);

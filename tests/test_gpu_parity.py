@@ -96,6 +96,10 @@ SMALL = [
     ("passq_cp4_small", dict(kind="pass_q", batch=2, cached=1000, new=300, cp=4, rank=0, interleave=8)),
     ("passq_cp3_il5_d64", dict(kind="pass_q", batch=3, cached=513, new=130, cp=3, rank=0, interleave=5, d=64,
                                hq=8, hkv=1)),
+    # a local shard of more than 2048 blocks: the prefill kernel reads the block table from HBM
+    # instead of staging it in LDS
+    ("passq_long_cache_table_in_hbm", dict(kind="pass_q", batch=1, cached=150000, new=70, cp=2, rank=1,
+                                           interleave=8, hq=4, hkv=2, d=64)),
     ("decode_cp2_small", dict(kind="decode", batch=16, len_range=(1, 3000), lengths=(), cp=2, rank=0,
                               interleave=8)),
     ("decode_cp4_d64_g8", dict(kind="decode", batch=9, len_range=(1, 700), lengths=(), cp=4, rank=0, interleave=3,
