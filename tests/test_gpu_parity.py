@@ -100,6 +100,8 @@ SMALL = [
     # instead of staging it in LDS
     ("passq_long_cache_table_in_hbm", dict(kind="pass_q", batch=1, cached=150000, new=70, cp=2, rank=1,
                                            interleave=8, hq=4, hkv=2, d=64)),
+    # odd GQA group: the paged prefill runs on the one-head-per-workgroup kernel
+    ("passq_cp2_g3", dict(kind="pass_q", batch=2, cached=700, new=150, cp=2, rank=1, interleave=4, hq=6, hkv=2)),
     ("decode_cp2_small", dict(kind="decode", batch=16, len_range=(1, 3000), lengths=(), cp=2, rank=0,
                               interleave=8)),
     ("decode_cp4_d64_g8", dict(kind="decode", batch=9, len_range=(1, 700), lengths=(), cp=4, rank=0, interleave=3,
