@@ -21,11 +21,13 @@
 //    assembled by two ds_read_b64_tr_b16 transposing reads, each giving a lane
 //    4 consecutive keys of its d column; the key order they produce matches
 //    the order in which the S^T accumulator lists a lane's keys.
-//  * With RB = 2 every K and V operand read from LDS feeds two MFMAs (one per
-//    32-row block), halving LDS traffic per FLOP and giving each wave 4 (QK)
-//    or 8 (PV) independent accumulation chains; the wave then holds ~400
-//    registers and runs alone on its SIMD. RB = 1 keeps two waves per SIMD for
-//    problems too small to fill the GPU with 256-row workgroups.
+//  * With RB = 2 every K and V operand read from LDS would feed two MFMAs (one
+//    per 32-row block), halving LDS traffic per FLOP; the wave then holds ~400
+//    registers and runs alone on its SIMD. That variant is compiled but not
+//    selected (kUseTwoRowBlocks): it measured slower than RB = 1, two 32-row
+//    waves per SIMD.
+// The two-group kernel (attn_pp.hip) serves every even GQA group; this one
+// serves odd groups.
 //  * K and V tiles of 64 keys are double-buffered in LDS, K one tile ahead of
 //    V, so the QK^T MFMAs of tile t+1 are issued while the softmax of tile t
 //    runs on the vector ALUs; the next tiles' global loads are in flight

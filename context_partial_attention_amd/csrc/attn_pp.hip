@@ -28,6 +28,14 @@
 // V^T operands are single 16-byte LDS reads, which run at about twice the
 // bandwidth of transposing reads; rows are padded so reads and writes are
 // bank-conflict free.
+//
+// One launch covers up to kMaxShards contiguous KV shards, each into its own
+// partial (a group is then (query tile, sequence, shard, KV head)), or with
+// MERGED one walk over the visible key tiles of every shard with a single
+// online softmax, which yields the exact merge of the shards' partials. With a
+// running accumulator (o_acc) the epilogue folds the partial into it instead
+// of writing it. An optional pre-pass (pp_schedule_kernel) orders the launch
+// heaviest query tile first. Paged shards (pass-Q prefill) take one shard.
 #include <climits>
 
 #include "cpa_internal.h"
