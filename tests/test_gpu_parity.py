@@ -209,7 +209,7 @@ def test_merged_walk_all_elements(cpa, wl, harness, name, changes):
 
 
 @pytest.mark.parametrize("name", ["qwen2.5_3b_cp2_rank0", "llama3_8b_128k_cp4_rank1"])
-def test_merged_walk_full_size_sampled(cpa, wl, harness, name):
+def test_fused_merge_full_size_sampled(cpa, wl, harness, name):
     w = wl.WORKLOADS[name]
     _say(f"case merged full-size {name}")
     inp = harness.build(w, device="cuda")
@@ -224,6 +224,13 @@ def test_merged_walk_full_size_sampled(cpa, wl, harness, name):
     ridx = torch.as_tensor(rows_, device="cuda")
     e = assert_close(f64(run.o[ridx]), f64(run.lse[ridx]), merged[0], merged[1], f"{name} merged walk")
     _say(f"  merged walk: max|dO|={e[0]:.2e} max|dLSE|={e[1]:.2e} over {len(rows_)} rows")
+    # the same shards folded in one at a time (running merge), bf16 output at the last step
+    run.o.fill_(float("nan"))
+    run.ring_accumulate()
+    torch.cuda.synchronize()
+    assert not torch.isnan(run.o).any() and torch.isfinite(run.lse).all()
+    e = assert_close(f64(run.o[ridx]), f64(run.lse[ridx]), merged[0], merged[1], f"{name} ring accumulate")
+    _say(f"  ring accumulate: max|dO|={e[0]:.2e} max|dLSE|={e[1]:.2e} over {len(rows_)} rows")
 
 
 def test_merged_walk_unsupported_cases(cpa, wl, harness):
