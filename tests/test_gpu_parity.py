@@ -147,6 +147,8 @@ MULTI = [
     ("cp2_r1_d64_g4", dict(lengths=(600, 129), batch=2, len_range=(), cp=2, rank=1, hq=8, hkv=2, d=64)),
     # eight shards (the most one launch takes), sequences shorter than 2cp: empty chunks and shards
     ("cp8_r5_tiny", dict(lengths=(3, 0, 17, 250, 1), batch=5, len_range=(), cp=8, rank=5)),
+    # GQA group of 6: three head pairs per KV head
+    ("cp2_r0_g6", dict(lengths=(450, 1200), batch=2, len_range=(), cp=2, rank=0, hq=12, hkv=2)),
 ]
 
 
@@ -231,6 +233,34 @@ def test_fused_merge_full_size_sampled(cpa, wl, harness, name):
     assert not torch.isnan(run.o).any() and torch.isfinite(run.lse).all()
     e = assert_close(f64(run.o[ridx]), f64(run.lse[ridx]), merged[0], merged[1], f"{name} ring accumulate")
     _say(f"  ring accumulate: max|dO|={e[0]:.2e} max|dLSE|={e[1]:.2e} over {len(rows_)} rows")
+
+
+def test_merged_walk_without_mask(cpa, wl, harness):
+    """No mask: every query sees every key of every shard; the one-walk merge
+    equals the oracle's merge of the unmasked partials."""
+    w = wl.scaled(wl.WORKLOADS["qwen2.5_3b_cp2_rank0"], name="merged_nomask", lengths=(333, 700), batch=2,
+                  len_range=(), cp=4, rank=1)
+    _say("case merged walk, no mask")
+    inp = harness.build(w, device="cuda")
+    st = inp["steps"]
+    o, l = cpa.partial_attn_merged(inp["q"], inp["q_pos"], inp["cu_q"], [s["k"] for s in st], [s["v"] for s in st],
+                                   [s["k_pos"] for s in st], [s["cu_k"] for s in st], inp["max_q"], w.scale,
+                                   causal=False)
+    torch.cuda.synchronize()
+    lens = inp["lens"]
+    mine = oracle.zigzag_partition(lens, w.cp, w.rank)
+    q_all = torch.cat([d[0] for d in inp["draws"]])
+    k_all = torch.cat([d[1] for d in inp["draws"]])
+    v_all = torch.cat([d[2] for d in inp["draws"]])
+    q = f64(q_all[torch.as_tensor(mine["src_index"], device="cuda")])
+    parts = []
+    for s in range(w.cp):
+        src = oracle.zigzag_partition(lens, w.cp, (w.rank - s) % w.cp)
+        idx = torch.as_tensor(src["src_index"], device="cuda")
+        parts.append(oracle.partial_attn(q, mine["positions"], mine["cu_seqlens"], f64(k_all[idx]), f64(v_all[idx]),
+                                         src["positions"], src["cu_seqlens"], w.scale, causal=False))
+    mo, ml = oracle.lse_merge([p[0] for p in parts], [p[1] for p in parts])
+    assert_close(f64(o), f64(l), mo, ml, "merged walk without mask")
 
 
 def test_merged_walk_unsupported_cases(cpa, wl, harness):
