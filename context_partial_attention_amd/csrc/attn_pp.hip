@@ -270,25 +270,24 @@ __global__ __launch_bounds__(kThreads, 1) void attn_pp_kernel(PPParams p) {
     if constexpr (PAGED) off[i] = (uint32_t)((r & 15) * D + c8 * 8);
     else off[i] = (uint32_t)(r * row_stride + c8 * 8);
   }
+  // paged: physical blocks of this thread's rows in the next slot's K tile
+  // and V tile, read from the block table one slot ahead of their loads
+  int pre_k[T::kChunks] = {};
+  int pre_v = 0;
   auto load_k = [&](const TileRef& tr, u32x4* regs) {
     const uint16_t* __restrict__ src = tr.k;
     const int j0 = tr.j0, n_end = tr.end;
     const bool last = j0 + kBN > n_end;
     if constexpr (PAGED) {
+      // physical blocks looked up one slot ahead (pre_k, uniform over the
+      // wave: its 4 rows of a piece never leave one 16-key block, clamped or
+      // not); rows past the visible range are clamped to its last row
       const int64_t slab = (int64_t)p.hkv * 16 * D;
-      const int* tab = p.block_table + (int64_t)seq * p.max_blocks;
-      auto tab_at = [&](int b) { return tab_in_lds ? tab_sh[b] : tab[b]; };
 #pragma unroll
       for (int i = 0; i < T::kChunks; ++i) {
-        const int r = r_first + i * T::kRowsPerPass;
-        if (!last) {
-          const int blk = __builtin_amdgcn_readfirstlane(tab_at(__builtin_amdgcn_readfirstlane((j0 + r) >> 4)));
-          regs[i] = *(const u32x4*)(src + (int64_t)blk * slab + (int64_t)kvh * 16 * D + off[i]);
-        } else {
-          const int j = min(j0 + r, n_end - 1);
-          const int blk = tab_at(j >> 4);
-          regs[i] = *(const u32x4*)(src + (int64_t)blk * slab + ((int64_t)kvh * 16 + (j & 15)) * D + c8 * 8);
-        }
+        const int j = last ? min(j0 + r_first + i * T::kRowsPerPass, n_end - 1) : j0 + r_first + i * T::kRowsPerPass;
+        const uint16_t* base = src + (int64_t)pre_k[i] * slab + (int64_t)kvh * 16 * D;
+        regs[i] = *(const u32x4*)(base + (j & 15) * D + c8 * 8);
       }
     } else {
       const uint16_t* b = src + ((int64_t)j0 * p.hkv + kvh) * D;
@@ -302,6 +301,19 @@ __global__ __launch_bounds__(kThreads, 1) void attn_pp_kernel(PPParams p) {
   };
   // V piece of thread tid < kVUnits: keys 2 kp, 2 kp + 1 of the tile, dims 8 dc .. 8 dc + 7
   const int v_kp = tid % (kBN / 2), v_dc = tid / (kBN / 2);
+  auto prefetch_tab = [&](int tk, int tv) {  // K tile tk, V tile tv
+    if constexpr (PAGED) {
+      const int* tab = p.block_table + (int64_t)seq * p.max_blocks;
+      auto tab_at = [&](int b) { return tab_in_lds ? tab_sh[b] : tab[b]; };
+      if (tk < n) {
+#pragma unroll
+        for (int i = 0; i < T::kChunks; ++i)
+          pre_k[i] = __builtin_amdgcn_readfirstlane(
+              tab_at(min(tk * kBN + r_first + i * T::kRowsPerPass, seg0_end - 1) >> 4));
+      }
+      if (tv >= 0 && tv < n && tid < T::kVUnits) pre_v = tab_at(min(tv * kBN + 2 * v_kp, seg0_end - 1) >> 4);
+    }
+  };
   auto load_v = [&](const TileRef& tr, u32x4* regs) {
     if (tid >= T::kVUnits) return;
     const uint16_t* __restrict__ vmat = tr.v;
@@ -310,8 +322,10 @@ __global__ __launch_bounds__(kThreads, 1) void attn_pp_kernel(PPParams p) {
     for (int r = 0; r < 2; ++r) {
       const int j = min(j0 + 2 * v_kp + r, n_end - 1);
       if constexpr (PAGED) {
-        const int blk = tab_in_lds ? tab_sh[j >> 4] : p.block_table[(int64_t)seq * p.max_blocks + (j >> 4)];
-        regs[r] = *(const u32x4*)(vmat + ((int64_t)blk * p.hkv + kvh) * 16 * D + (j & 15) * D + v_dc * 8);
+        // keys 2 kp and 2 kp + 1 (an even key and the next, or both clamped to
+        // the last visible key) lie in one 16-key block, looked up one slot
+        // ahead (pre_v)
+        regs[r] = *(const u32x4*)(vmat + ((int64_t)pre_v * p.hkv + kvh) * 16 * D + (j & 15) * D + v_dc * 8);
       } else {
         regs[r] = *(const u32x4*)(vmat + ((int64_t)j * p.hkv + kvh) * D + v_dc * 8);
       }
@@ -363,6 +377,9 @@ __global__ __launch_bounds__(kThreads, 1) void attn_pp_kernel(PPParams p) {
         *(uint32_t*)(vt + (2 * e + 1) * T::kVStride) = (w0 >> 16) | (w1 & 0xffff0000u);
       }
     }
+    // paged: the blocks of the next slot (K(t+1), V(t)), read here at the end
+    // of a phase, not on the way into the matrix work
+    prefetch_tab(t + 1, t);
   };
 
   // ---- per-wave state
@@ -511,6 +528,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_pp_kernel(PPParams p) {
   };
 
   if (n > 0) {
+    prefetch_tab(0, -1);
     load_slot(0);
     store_slot(0);
     __syncthreads();
