@@ -76,7 +76,7 @@ def merge_bytes(w, rows: int, n_parts: int, out_bytes: int) -> int:
 # ------------------------------------------------------------------ GPU timing
 
 
-def bench_workload(name: str, steps: int, warmup: int) -> dict:
+def bench_workload(name: str, steps: int, warmup: int, next_rows: bool = True) -> dict:
     import torch
 
     from context_partial_attention_amd import harness
@@ -184,7 +184,7 @@ def bench_workload(name: str, steps: int, warmup: int) -> dict:
         del rk
     if w.kind == "pass_kv":
         res["seq_lens"] = inp["lens"]
-        if w.dtype == torch.bfloat16 and (w.hq // w.hkv) % 2 == 0:
+        if next_rows and w.dtype == torch.bfloat16 and (w.hq // w.hkv) % 2 == 0:
             # next row (fused merge): every resident shard walked in one launch,
             # the merged (O, LSE) written directly; same algorithmic work
             fw_ms = per_launch_ms(run.merged_walk)
@@ -294,6 +294,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workloads", type=str, default=",".join(DEFAULT_WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-next-rows", action="store_true",
+                    help="skip the fused-merge walk and running-merge timings (profiling the partials kernel alone)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain device-to-device copy of 256 MiB (x4) to scale HBM byte counters")
     args = ap.parse_args()
@@ -324,7 +326,7 @@ def main():
     results = {}
     for name in names:
         log(f"[bench] {name}: {args.warmup} warmup + {args.steps} timed steps")
-        results[name] = bench_workload(name, args.steps, args.warmup)
+        results[name] = bench_workload(name, args.steps, args.warmup, next_rows=not args.no_next_rows)
         log(f"[bench] {name}: {json.dumps({k: v for k, v in results[name].items() if k != 'description'})}")
     h = results[HEADLINE]
     # dominant kernel of the headline: the batched partial-attention launch
