@@ -169,6 +169,10 @@ def test_multi_shard_call_validation_before_gpu(cpa):
     assert n.value >= 29 * 4 * 2 * 4 and n.value % 256 == 0  # one int per (query tile, sequence, shard)
     assert lib.cpa_partial_attn_multi_workspace(2, 4, 0, ctypes.byref(n)) == 0 and n.value == 0
     assert lib.cpa_partial_attn_multi_workspace(9, 4, 100, ctypes.byref(n)) == -1
+    # the ordering pre-pass sorts at most 8192 (query tile, sequence, shard) units; past that the
+    # launch runs in index order and asks for no workspace
+    assert lib.cpa_partial_attn_multi_workspace(8, 64, 2048, ctypes.byref(n)) == 0 and n.value == 8192 * 4
+    assert lib.cpa_partial_attn_multi_workspace(8, 64, 2049, ctypes.byref(n)) == 0 and n.value == 0
 
 
 def test_merged_call_validation_before_gpu(cpa):
