@@ -144,6 +144,32 @@ def bench_workload(name: str, steps: int, warmup: int, next_rows: bool = True) -
     part_ms = [per_launch_ms(f) for f in launches]
     merge_ms = per_launch_ms(run.merge)
 
+    # (3) cold caches for the HBM-bound launches (merge; decode partial): a
+    # read of a 1 GiB buffer before every launch evicts the 256 MB Infinity
+    # Cache and the L2s without leaving dirty lines behind. Timed as the
+    # difference between `steps` rounds of (flush, launch) and of the flush
+    # alone, both back to back between one pair of events.
+    flush_buf = torch.ones(1 << 28, dtype=torch.float32, device=stream.device)
+    flush_out = torch.empty((), dtype=torch.float32, device=stream.device)
+
+    def cold_launch_ms(f):
+        def rounds(with_f):
+            a, b = ev(), ev()
+            torch.cuda.synchronize()
+            a.record(stream)
+            for _ in range(steps):
+                torch.sum(flush_buf, dim=0, out=flush_out)
+                if with_f:
+                    f()
+            b.record(stream)
+            torch.cuda.synchronize()
+            return a.elapsed_time(b) / steps
+
+        rounds(True)
+        return max(rounds(True) - rounds(False), 1e-6)
+
+    merge_cold_ms = cold_launch_ms(run.merge)
+
     rows = inp["q"].shape[0] * w.hq
     mbytes = merge_bytes(w, rows, w.cp, 2 if run.merged_dtype == torch.bfloat16 else 4)
     res = {
@@ -156,6 +182,10 @@ def bench_workload(name: str, steps: int, warmup: int, next_rows: bool = True) -
         "merge_ms": merge_ms,
         "merge_GBps": mbytes / (merge_ms * 1e-3) / 1e9,
         "merge_hbm_frac": mbytes / (merge_ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
+        "merge_bytes": int(mbytes),
+        "merge_cold_ms": merge_cold_ms,
+        "merge_cold_GBps": mbytes / (merge_cold_ms * 1e-3) / 1e9,
+        "merge_cold_hbm_frac": mbytes / (merge_cold_ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
     }
     if w.kind == "pass_kv":
         pairs = [pass_kv_pairs(inp, i) for i in own]
@@ -179,6 +209,10 @@ def bench_workload(name: str, steps: int, warmup: int, next_rows: bool = True) -
         res["partial_bytes"] = int(part_bytes)
         res["partial_GBps"] = part_bytes / (res["partial_ms"][0] * 1e-3) / 1e9
         res["partial_hbm_frac"] = res["partial_GBps"] / PEAK_HBM_GBS
+        cold = cold_launch_ms(launches[0])
+        res["partial_cold_ms"] = cold
+        res["partial_cold_GBps"] = part_bytes / (cold * 1e-3) / 1e9
+        res["partial_cold_hbm_frac"] = res["partial_cold_GBps"] / PEAK_HBM_GBS
         res["GBps"] = (part_bytes + mbytes) / (res["ms_per_step"] * 1e-3) / 1e9
         res["hbm_frac"] = res["GBps"] / PEAK_HBM_GBS
         del rk
@@ -196,7 +230,7 @@ def bench_workload(name: str, steps: int, warmup: int, next_rows: bool = True) -
             ra_ms = per_launch_ms(run.ring_accumulate)
             res["ring_accumulate_ms"] = ra_ms
             res["ring_accumulate_TFLOPs"] = sum(flops) / (ra_ms * 1e-3) / 1e12
-    del run, inp
+    del run, inp, flush_buf, flush_out
     torch.cuda.empty_cache()
     return res
 
