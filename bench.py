@@ -141,6 +141,18 @@ def bench_workload(name: str, steps: int, warmup: int, next_rows: bool = True) -
         torch.cuda.synchronize()
         return a.elapsed_time(b) / steps
 
+    # per-replay spread: each replay between its own pair of events (these
+    # include the dispatch gap an event opens, so they sit a little above
+    # the mean of region (1))
+    pairs_ev = [(ev(), ev()) for _ in range(steps)]
+    torch.cuda.synchronize()
+    for a, b in pairs_ev:
+        a.record(stream)
+        graph.replay()
+        b.record(stream)
+    torch.cuda.synchronize()
+    rep_ms = [a.elapsed_time(b) for a, b in pairs_ev]
+
     part_ms = [per_launch_ms(f) for f in launches]
     merge_ms = per_launch_ms(run.merge)
 
@@ -178,6 +190,8 @@ def bench_workload(name: str, steps: int, warmup: int, next_rows: bool = True) -
         "steps": steps,
         "ms_per_step": wall_ms / steps,
         "gpu_ms_per_step": gpu_ms / steps,
+        "step_ms_median_own_events": float(np.median(rep_ms)),
+        "step_ms_min_own_events": float(np.min(rep_ms)),
         "partial_ms": part_ms,
         "merge_ms": merge_ms,
         "merge_GBps": mbytes / (merge_ms * 1e-3) / 1e9,
@@ -321,6 +335,36 @@ def cpu_baseline(name: str, budget_s: float = 10.0) -> dict:
 # ------------------------------------------------------------------ main
 
 
+def environment() -> dict:
+    """Software versions, device and the clocks the driver reports (best effort)."""
+    import subprocess
+
+    import torch
+
+    props = torch.cuda.get_device_properties(0)
+    env = {
+        "torch": torch.__version__,
+        "hip": torch.version.hip,
+        "device": props.name,
+        "arch": getattr(props, "gcnArchName", None),
+        "compute_units": props.multi_processor_count,
+        "host_cpus": len(os.sched_getaffinity(0)),
+    }
+    try:
+        out = subprocess.run(["rocm-smi", "--showclocks", "--json"], capture_output=True, text=True, timeout=30)
+        clocks = json.loads(out.stdout)
+        card = next(iter(clocks.values()))
+        env["clocks"] = {k: v for k, v in card.items() if "clock" in k.lower()}
+    except Exception as e:  # reported, not fatal: the numbers above do not depend on it
+        env["clocks"] = f"unavailable ({type(e).__name__})"
+    try:
+        with open("/opt/rocm/.info/version") as f:
+            env["rocm"] = f.read().strip()
+    except OSError:
+        env["rocm"] = None
+    return env
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -416,6 +460,7 @@ def main():
             "ring_accumulate_TFLOPs": h.get("ring_accumulate_TFLOPs"),
         },
     }
+    line["environment"] = environment()
     if not args.no_cpu_baseline:
         log("[bench] cpu baseline (oracle) ...")
         line["cpu_baseline"] = cpu_baseline(HEADLINE)
