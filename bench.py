@@ -336,8 +336,10 @@ def cpu_baseline(name: str, budget_s: float = 10.0) -> dict:
 
 
 def environment() -> dict:
-    """Software versions, device and the clocks the driver reports (best effort)."""
-    import subprocess
+    """Software versions, device, and the shader and memory clock levels the
+    driver lists as current in sysfs (read as files: no helper program is
+    started from this GPU process)."""
+    import glob
 
     import torch
 
@@ -350,13 +352,15 @@ def environment() -> dict:
         "compute_units": props.multi_processor_count,
         "host_cpus": len(os.sched_getaffinity(0)),
     }
-    try:
-        out = subprocess.run(["rocm-smi", "--showclocks", "--json"], capture_output=True, text=True, timeout=30)
-        clocks = json.loads(out.stdout)
-        card = next(iter(clocks.values()))
-        env["clocks"] = {k: v for k, v in card.items() if "clock" in k.lower()}
-    except Exception as e:  # reported, not fatal: the numbers above do not depend on it
-        env["clocks"] = f"unavailable ({type(e).__name__})"
+    clocks = {}
+    for path in sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_[sm]clk")):
+        try:
+            with open(path) as f:
+                cur = [ln.split(":", 1)[1].strip().rstrip("*").strip() for ln in f if ln.rstrip().endswith("*")]
+            clocks[path.split("/")[4] + "/" + path.rsplit("_", 1)[1]] = cur[0] if cur else None
+        except (OSError, IndexError):
+            continue
+    env["clocks_current_level"] = clocks or None
     try:
         with open("/opt/rocm/.info/version") as f:
             env["rocm"] = f.read().strip()
