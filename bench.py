@@ -108,11 +108,16 @@ def bench_workload(name: str, steps: int, warmup: int, next_rows: bool = True) -
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
-    # the step runs as one captured HIP graph (its kernels are plain launches
-    # on the stream: no memsets, no allocations), which removes the host
-    # launch overhead between its kernels
-    graph = run.capture(step)
-    for _ in range(warmup):
+    # the step runs as a captured HIP graph (its kernels are plain launches on
+    # the stream: no memsets, no allocations), which removes the host launch
+    # overhead between its kernels. The timed loop replays a graph holding
+    # `per_graph` consecutive steps (the largest divisor of `steps` up to 64),
+    # as a model's forward pass holds its attention layers in one graph: each
+    # graph launch opens a dispatch gap of ~8-20 us on the stream.
+    per_graph = max(d for d in range(1, 65) if steps % d == 0)
+    graph1 = run.capture(step)
+    graph = graph1 if per_graph == 1 else run.capture(lambda: [step() for _ in range(per_graph)])
+    for _ in range(max(1, warmup // per_graph)):
         graph.replay()
     torch.cuda.synchronize()
 
@@ -123,7 +128,7 @@ def bench_workload(name: str, steps: int, warmup: int, next_rows: bool = True) -
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     g0.record(stream)
-    for _ in range(steps):
+    for _ in range(steps // per_graph):
         graph.replay()
     g1.record(stream)
     torch.cuda.synchronize()
@@ -141,14 +146,14 @@ def bench_workload(name: str, steps: int, warmup: int, next_rows: bool = True) -
         torch.cuda.synchronize()
         return a.elapsed_time(b) / steps
 
-    # per-replay spread: each replay between its own pair of events (these
-    # include the dispatch gap an event opens, so they sit a little above
-    # the mean of region (1))
+    # per-step spread: the one-step graph replayed between its own pair of
+    # events each time (these include the graph launch and the dispatch gap
+    # an event opens)
     pairs_ev = [(ev(), ev()) for _ in range(steps)]
     torch.cuda.synchronize()
     for a, b in pairs_ev:
         a.record(stream)
-        graph.replay()
+        graph1.replay()
         b.record(stream)
     torch.cuda.synchronize()
     rep_ms = [a.elapsed_time(b) for a, b in pairs_ev]
@@ -190,6 +195,7 @@ def bench_workload(name: str, steps: int, warmup: int, next_rows: bool = True) -
         "steps": steps,
         "ms_per_step": wall_ms / steps,
         "gpu_ms_per_step": gpu_ms / steps,
+        "steps_per_graph": per_graph,
         "step_ms_median_own_events": float(np.median(rep_ms)),
         "step_ms_min_own_events": float(np.min(rep_ms)),
         "partial_ms": part_ms,
@@ -438,8 +444,8 @@ def main():
             "hq": 16,
             "hkv": 2,
             "d": 128,
-            "step": "2 pass-KV partial attentions (one batched launch) + 2-way LSE merge (bf16 out), "
-                    "replayed as one captured HIP graph",
+            "step": "2 pass-KV partial attentions (one batched launch) + 2-way LSE merge (bf16 out); "
+                    f"the timed loop replays a captured HIP graph of {h['steps_per_graph']} consecutive steps",
         },
         "roofline": {
             "kernel": "attn_pp_kernel<128, contiguous, fp32 out, partials>, both pass-KV steps in one launch "

@@ -21,14 +21,9 @@
 // conflict and group 1's matrix work stalls behind group 0's softmax.
 //
 // LDS holds two slots; slot t carries K(t), V(t-1) and the key positions of
-// tile t and is read in phases 2t and 2t+1. Only the waves in phase B stage
-// tiles: each group owns half of every slot (K rows 32g..32g+31, the V dims
-// of its half, and for group 0 the key positions) and, at the start of each
-// of its B phases, writes the half it loaded two phases before, then issues
-// the loads of its half of the next slot. Group 1 writes its half of slot t
-// at the start of phase 2t-2, group 0 at the start of 2t-1; the buffer was
-// last read in phase 2t-3. The waves feeding the matrix cores thus issue no
-// global loads and no LDS writes. V is transposed on its way into LDS
+// tile t and is read in phases 2t and 2t+1. Its global loads are issued at
+// the start of phase 2t-2 and written to LDS at the end of phase 2t-1, so
+// every load has two phases to arrive. V is transposed on its way into LDS
 // (d-major, keys permuted to match the S^T accumulator order), so both K and
 // V^T operands are single 16-byte LDS reads, which run at about twice the
 // bandwidth of transposing reads; rows are padded so reads and writes are
@@ -63,16 +58,14 @@ struct PPTile {
   static constexpr int kVStride = kBN + 8;
   static constexpr int kKElems = kBN * kKStride;
   static constexpr int kVElems = D * kVStride;
-  // a group's half of a slot: (key pair, 8 dims) pieces of half the V dims,
-  // and 16-byte pieces of half the K rows
-  static constexpr int kVUnits = (kBN / 2) * (D / 16);
+  static constexpr int kVUnits = (kBN / 2) * (D / 8);  // (key pair, 8 dims) pieces of a V tile
   static constexpr int kSlotElems = kKElems + kVElems;
   static constexpr int kChunksPerRow = D / 8;
-  static constexpr int kChunks = (kBN / 2) * kChunksPerRow / (kThreads / 2);  // K pieces per thread
-  static constexpr int kRowsPerPass = (kThreads / 2) / kChunksPerRow;
-  static_assert(kChunks >= 1 && kChunks * (kThreads / 2) == (kBN / 2) * kChunksPerRow, "tile must split evenly");
+  static constexpr int kChunks = kBN * kChunksPerRow / kThreads;  // 16-byte pieces per thread per matrix
+  static constexpr int kRowsPerPass = kThreads / kChunksPerRow;
+  static_assert(kChunks >= 1 && kChunks * kThreads == kBN * kChunksPerRow, "tile must split evenly");
   static_assert(kRowsPerPass % 16 == 0 && 16 % (64 / kChunksPerRow) == 0, "wave rows must share a block");
-  static_assert(kVUnits <= kThreads / 2, "one V piece per thread at most");
+  static_assert(kVUnits <= kThreads, "one V piece per thread at most");
 };
 
 struct PPParams {
@@ -266,11 +259,9 @@ __global__ __launch_bounds__(kThreads, 1) void attn_pp_kernel(PPParams p) {
     for (int kk = 0; kk < D / 16; ++kk) qf[kk] = *(const bf16x8*)(src + 16 * kk);
   }
 
-  // ---- slot staging (each group its half): K piece i of a thread covers
-  // row r_first + i*kRowsPerPass of the tile, in the group's 32 rows
-  const int gt = tid & (kThreads / 2 - 1);  // thread index within the group
-  const int c8 = gt % T::kChunksPerRow;
-  const int r_first = (kBN / 2) * gp + gt / T::kChunksPerRow;
+  // ---- slot staging: piece i of a matrix covers row r_first + i*kRowsPerPass
+  const int c8 = tid % T::kChunksPerRow;
+  const int r_first = tid / T::kChunksPerRow;
   const int64_t row_stride = (int64_t)p.hkv * D;
   uint32_t off[T::kChunks];
 #pragma unroll
@@ -308,9 +299,8 @@ __global__ __launch_bounds__(kThreads, 1) void attn_pp_kernel(PPParams p) {
       }
     }
   };
-  // V piece of thread gt < kVUnits: keys 2 kp, 2 kp + 1 of the tile, dims 8 dc .. 8 dc + 7
-  // (32 consecutive threads take the 32 key pairs of one dc: conflict-free writes)
-  const int v_kp = gt % (kBN / 2), v_dc = gp * (D / 16) + gt / (kBN / 2);
+  // V piece of thread tid < kVUnits: keys 2 kp, 2 kp + 1 of the tile, dims 8 dc .. 8 dc + 7
+  const int v_kp = tid % (kBN / 2), v_dc = tid / (kBN / 2);
   auto prefetch_tab = [&](int tk, int tv) {  // K tile tk, V tile tv
     if constexpr (PAGED) {
       const int* tab = p.block_table + (int64_t)seq * p.max_blocks;
@@ -321,11 +311,11 @@ __global__ __launch_bounds__(kThreads, 1) void attn_pp_kernel(PPParams p) {
           pre_k[i] = __builtin_amdgcn_readfirstlane(
               tab_at(min(tk * kBN + r_first + i * T::kRowsPerPass, seg0_end - 1) >> 4));
       }
-      if (tv >= 0 && tv < n && gt < T::kVUnits) pre_v = tab_at(min(tv * kBN + 2 * v_kp, seg0_end - 1) >> 4);
+      if (tv >= 0 && tv < n && tid < T::kVUnits) pre_v = tab_at(min(tv * kBN + 2 * v_kp, seg0_end - 1) >> 4);
     }
   };
   auto load_v = [&](const TileRef& tr, u32x4* regs) {
-    if (gt >= T::kVUnits) return;
+    if (tid >= T::kVUnits) return;
     const uint16_t* __restrict__ vmat = tr.v;
     const int j0 = tr.j0, n_end = tr.end;
 #pragma unroll
@@ -366,7 +356,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_pp_kernel(PPParams p) {
     if (t < n) {
       tr = tile_ref(t);
       load_k(tr, kreg);
-      if (gp == 0 && tid < kBN) kp_reg = key_pos(tr);
+      if (tid < kBN) kp_reg = key_pos(tr);
     }
     if (t >= 1) load_v(MERGED ? prev_tr : tile_ref(t - 1), vreg);
     prev_tr = tr;
@@ -375,9 +365,9 @@ __global__ __launch_bounds__(kThreads, 1) void attn_pp_kernel(PPParams p) {
     const int s = t & 1;
     if (t < n) {
       store_tile(kslot(s), T::kKStride, kreg);
-      if (gp == 0 && tid < kBN) kpos_sh[s][tid] = kp_reg;
+      if (tid < kBN) kpos_sh[s][tid] = kp_reg;
     }
-    if (t >= 1 && gt < T::kVUnits) {
+    if (t >= 1 && tid < T::kVUnits) {
       // transpose the key pair into 8 dim rows: one 4-byte (key, key+1) pair per row
       uint16_t* vt = vslot(s) + (8 * v_dc) * T::kVStride + pp_v_slot(2 * v_kp);
 #pragma unroll
@@ -387,6 +377,9 @@ __global__ __launch_bounds__(kThreads, 1) void attn_pp_kernel(PPParams p) {
         *(uint32_t*)(vt + (2 * e + 1) * T::kVStride) = (w0 >> 16) | (w1 & 0xffff0000u);
       }
     }
+    // paged: the blocks of the next slot (K(t+1), V(t)), read here at the end
+    // of a phase, not on the way into the matrix work
+    prefetch_tab(t + 1, t);
   };
 
   // ---- per-wave state
@@ -398,10 +391,6 @@ __global__ __launch_bounds__(kThreads, 1) void attn_pp_kernel(PPParams p) {
   constexpr float kTau = 8.f;  // lazy-rescale threshold (log2 units)
   f32x16 s0 = {}, s1 = {};  // S(t) after phase A, P(t) in fp32 after phase B
   bool p_valid = false;     // s0/s1 hold P of the previous tile for this wave
-  // first-key test and last key position of the tile, read in phase A under
-  // the matrix work, for the softmax phase that follows it
-  bool b_valid = false;
-  int b_kplast = 0;
 
   const int k_lane = lr * T::kKStride + 8 * lc;
   const int v_lane = lr * T::kVStride + 8 * lc;  // V^T rows (dims) lr (+32 db), slots 16 kst + 8 lc
@@ -424,8 +413,6 @@ __global__ __launch_bounds__(kThreads, 1) void attn_pp_kernel(PPParams p) {
     const int s = t & 1;
     const bool do_pv = t >= 1 && p_valid;
     const bool do_qk = t < n && __builtin_amdgcn_readfirstlane(kpos_sh[s][0]) <= wave_qmax;
-    b_valid = do_qk;
-    b_kplast = __builtin_amdgcn_readfirstlane(kpos_sh[s][kBN - 1]);
     const uint16_t* vs = vslot(s) + v_lane;
     const uint16_t* ks = kslot(s) + k_lane;
     constexpr int kPV = 4 * (D / 32), kQK = D / 8, kRing = 6;
@@ -509,10 +496,10 @@ __global__ __launch_bounds__(kThreads, 1) void attn_pp_kernel(PPParams p) {
   auto phase_b = [&](int t) {
     __builtin_amdgcn_s_setprio(0);
     const int* kp = kpos_sh[t & 1];
-    p_valid = b_valid;
+    p_valid = __builtin_amdgcn_readfirstlane(kp[0]) <= wave_qmax;
     if (!p_valid) return;
     // accumulator element v of this lane holds key 8*(v/4) + 4*lc + v%4 (+32 for s1)
-    if (b_kplast > wave_qmin) {
+    if (__builtin_amdgcn_readfirstlane(kp[kBN - 1]) > wave_qmin) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
         const int key = 8 * (v >> 2) + 4 * lc + (v & 3);
@@ -523,13 +510,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_pp_kernel(PPParams p) {
     float mx = fmaxf(s0[0], s1[0]);
 #pragma unroll
     for (int v = 1; v < 16; ++v) mx = pp_max3(mx, s0[v], s1[v]);
-    {
-      // the row's other 32 keys sit in lane +-32: v_permlane32_swap brings them
-      // over in the vector ALU (a ds_bpermute would queue in LDS behind the
-      // other group's operand reads)
-      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
-      mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])) * sl2;
-    }
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * sl2;
     if (__ballot(mx > m_run + kTau) != 0) {
       const float m_new = fmaxf(m_run, mx);
       const float alpha = (m_new == kNegInf) ? 1.f : hw_exp2(m_run - m_new);
@@ -547,30 +528,21 @@ __global__ __launch_bounds__(kThreads, 1) void attn_pp_kernel(PPParams p) {
   };
 
   if (n > 0) {
-    // each group: its half of slot 0 in LDS, its half of slot 1 in registers
     prefetch_tab(0, -1);
     load_slot(0);
     store_slot(0);
-    prefetch_tab(1, 0);
-    load_slot(1);
-    prefetch_tab(2, 1);  // table entries for the next load (paged)
     __syncthreads();
     // phases 0 .. 2n+1; group 0 runs A(t) in phase 2t and B(t) in 2t+1,
-    // group 1 one phase later (its phase -1, before A(0), is idle)
+    // group 1 one phase later; slot t+1 is loaded during phases 2t, 2t+1
     for (int ph = 0; ph <= 2 * n + 1; ++ph) {
+      const int t_ld = ph >> 1;
+      if (!(ph & 1) && t_ld + 1 <= n) load_slot(t_ld + 1);
       const int q = ph - gp;  // this group's own phase index
-      if (q & 1) {  // a B phase (or group 1's idle phase 0): stage slot u, load u+1
-        const int u = (ph >> 1) + 1;
-        if (u <= n) store_slot(u);
-        if (u + 1 <= n) {
-          load_slot(u + 1);
-          prefetch_tab(u + 2, u + 1);
-        }
-      }
       if (q >= 0 && q <= 2 * n) {
         if (!(q & 1)) phase_a(q >> 1);
         else phase_b(q >> 1);
       }
+      if ((ph & 1) && t_ld + 1 <= n) store_slot(t_ld + 1);
       lds_barrier();
     }
   }
