@@ -48,6 +48,11 @@ constexpr int kBN = 64;        // keys per tile
 constexpr int kRows = 128;     // query rows per workgroup (per head)
 constexpr int kThreads = 512;  // 8 waves
 constexpr int kTabCap = 2048;  // paged: block-table entries of a workgroup staged in LDS (8 KiB)
+// launch-order entry: unit index in the low bits, its visible key-tile count
+// above them (kOrderWorkUnknown when it does not fit)
+constexpr int kOrderUnitBits = 13;
+constexpr int kOrderUnitMask = (1 << kOrderUnitBits) - 1;
+constexpr int kOrderWorkUnknown = (1 << (31 - kOrderUnitBits)) - 1;
 
 template <int D>
 struct PPTile {
@@ -136,8 +141,15 @@ __global__ __launch_bounds__(kThreads, 1) void attn_pp_kernel(PPParams p) {
   const int grow = rest / pairs;
   int grp = grow * 8 + ((xcd - grow) & 7);
   if (grp >= p.n_groups) return;
+  // visible key tiles of the unit as the launch-order pre-pass counted them
+  // (-1: not known, search below)
+  int pre_n = -1;
   if constexpr (!PAGED) {
-    if (p.order) grp = p.order[grp / p.hkv] * p.hkv + grp % p.hkv;
+    if (p.order) {
+      const int e = p.order[grp / p.hkv];
+      grp = (e & kOrderUnitMask) * p.hkv + grp % p.hkv;
+      if (!MERGED && (e >> kOrderUnitBits) != kOrderWorkUnknown) pre_n = e >> kOrderUnitBits;
+    }
   }
   // group = ((tile_desc * num_seqs + seq) * n_shards + shard) * hkv + kvh
   // (no shard term when MERGED: one group walks every shard): the heaviest
@@ -201,8 +213,17 @@ __global__ __launch_bounds__(kThreads, 1) void attn_pp_kernel(PPParams p) {
   __shared__ int tab_sh[PAGED ? kTabCap : 1];
   bool tab_in_lds = false;
   if constexpr (!MERGED) {
-    seg_range(shard, seg0_ka, seg0_end);
-    n = seg0_end > seg0_ka ? (seg0_end - seg0_ka + kBN - 1) / kBN : 0;
+    if (!PAGED && pre_n >= 0) {
+      // the pre-pass counted the key tiles whose first key some row sees; the
+      // last of them may hold keys past the visible end, which the per-key
+      // mask removes like any other masked key
+      seg0_ka = p.cu_k[shard][seq];
+      seg0_end = min(seg0_ka + pre_n * kBN, p.cu_k[shard][seq + 1]);
+      n = pre_n;
+    } else {
+      seg_range(shard, seg0_ka, seg0_end);
+      n = seg0_end > seg0_ka ? (seg0_end - seg0_ka + kBN - 1) / kBN : 0;
+    }
     if constexpr (PAGED) {
       const int nb = (seg0_end + 15) >> 4;  // <= max_blocks (seg0_end is clamped to it)
       tab_in_lds = nb <= kTabCap;
@@ -622,14 +643,17 @@ __global__ __launch_bounds__(kThreads, 1) void attn_pp_kernel(PPParams p) {
 // every unit's key tiles (a binary search over the first positions of the
 // shard's key tiles) and counting-sorts the units by it, descending. Units
 // of equal work keep no particular order; the results do not depend on it.
+// Each entry also carries the unit's count, so the attention kernel starts
+// its first tile loads without searching the key positions itself.
 constexpr int kSchedThreads = 1024;
 constexpr int kSchedBuckets = 4096;
 constexpr int kSchedMaxUnits = 8192;
 
 __global__ __launch_bounds__(kSchedThreads) void pp_schedule_kernel(PPParams p, int n_units, int merged,
                                                                      int* order) {
+  static_assert(kSchedMaxUnits <= 1 << kOrderUnitBits, "unit index must fit its field");
   __shared__ int bucket[kSchedBuckets];
-  __shared__ uint16_t key_sh[kSchedMaxUnits];
+  __shared__ int work_sh[kSchedMaxUnits];
   __shared__ int wave_tot[kSchedThreads / 64];
   const int tid = threadIdx.x;
   for (int b = tid; b < kSchedBuckets; b += kSchedThreads) bucket[b] = 0;
@@ -665,9 +689,8 @@ __global__ __launch_bounds__(kSchedThreads) void pp_schedule_kernel(PPParams p, 
         }
       }
     }
-    const int key = min(work, kSchedBuckets - 1);
-    key_sh[u] = (uint16_t)key;
-    atomicAdd(&bucket[key], 1);
+    work_sh[u] = work;
+    atomicAdd(&bucket[min(work, kSchedBuckets - 1)], 1);
   }
   __syncthreads();
   // exclusive scan over the buckets in descending key order: thread t owns
@@ -696,7 +719,11 @@ __global__ __launch_bounds__(kSchedThreads) void pp_schedule_kernel(PPParams p, 
     base += c[j];
   }
   __syncthreads();
-  for (int u = tid; u < n_units; u += kSchedThreads) order[atomicAdd(&bucket[key_sh[u]], 1)] = u;
+  for (int u = tid; u < n_units; u += kSchedThreads) {
+    const int work = work_sh[u];
+    order[atomicAdd(&bucket[min(work, kSchedBuckets - 1)], 1)] =
+        u | (min(work, kOrderWorkUnknown) << kOrderUnitBits);
+  }
 }
 
 template <int D, bool PAGED, bool OUT_BF16, bool MERGED = false>

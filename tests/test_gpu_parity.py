@@ -138,6 +138,14 @@ def test_small_bf16_output_and_no_mask(cpa, wl, harness):
     ro, rl = oracle.partial_attn(q, mine["positions"], mine["cu_seqlens"], k, v, src["positions"],
                                  src["cu_seqlens"], w.scale, causal=False)
     assert_close(f64(o), f64(l), ro, rl, "no-mask bf16-out")
+    # the batched call with its launch order (whose entries carry each unit's
+    # key-tile count) gives the same bits as the single call without a mask
+    ws = torch.empty(cpa.partial_attn_multi_workspace(1, 2, inp["max_q"]), dtype=torch.uint8, device="cuda")
+    (om,), (lm,) = cpa.partial_attn_multi(inp["q"], inp["q_pos"], inp["cu_q"], [st["k"]], [st["v"]], [st["k_pos"]],
+                                          [st["cu_k"]], inp["max_q"], w.scale, causal=False,
+                                          out_dtype=torch.bfloat16, workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(om, o) and torch.equal(lm, l), "no-mask batched launch differs from the single call"
 
 
 MULTI = [
