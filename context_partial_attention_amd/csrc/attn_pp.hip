@@ -21,13 +21,14 @@
 // conflict and group 1's matrix work stalls behind group 0's softmax.
 //
 // LDS holds two slots; slot t carries K(t), V(t-1) and the key positions of
-// tile t and is read in phases 2t and 2t+1. Its global loads are issued at
-// the start of phase 2t-2 and written to LDS at the end of phase 2t-1, so
-// every load has two phases to arrive. V is transposed on its way into LDS
-// (d-major, keys permuted to match the S^T accumulator order), so both K and
-// V^T operands are single 16-byte LDS reads, which run at about twice the
-// bandwidth of transposing reads; rows are padded so reads and writes are
-// bank-conflict free.
+// tile t and is read in phases 2t and 2t+1. Its K and V tiles travel from
+// global memory straight into LDS (gfx950's 16-byte global->LDS loads, no
+// registers and no LDS write instructions in the waves): they are issued at
+// the start of phase 2t-2 and waited for at the end of phase 2t-1, so every
+// load has two phases to arrive. Both tiles are row-major with the 16-byte
+// pieces of each row swizzled so that the K operand reads (16 bytes) and the
+// transposing V^T operand reads (ds_read_b64_tr_b16, which hand each lane 4
+// consecutive keys of one dim) are bank-conflict free.
 //
 // One launch covers up to kMaxShards contiguous KV shards, each into its own
 // partial (a group is then (query tile, sequence, shard, KV head)), or with
@@ -56,21 +57,27 @@ constexpr int kOrderWorkUnknown = (1 << (31 - kOrderUnitBits)) - 1;
 
 template <int D>
 struct PPTile {
-  static constexpr int kKStride = D + 8;   // 16-byte K reads: 4 banks apart per row
-  // V is stored transposed (d-major, one row per head dim holding the tile's
-  // 64 keys): rows 36 dwords apart make the 16-byte operand reads and the
-  // 4-byte key-pair writes bank-conflict free
-  static constexpr int kVStride = kBN + 8;
-  static constexpr int kKElems = kBN * kKStride;
-  static constexpr int kVElems = D * kVStride;
-  static constexpr int kVUnits = (kBN / 2) * (D / 8);  // (key pair, 8 dims) pieces of a V tile
+  // K and V tiles are stored row-major ([64 keys][D], no padding) as the
+  // global->LDS loads write them: each load instruction fills 1 KiB of LDS
+  // with 16 bytes per lane in lane order, and which 16-byte piece of a row a
+  // lane fetches sets the layout. Pieces are swizzled within a row (the
+  // piece index is XORed with swz(row)) so that both operand reads are
+  // bank-conflict free: 16 lanes reading one piece column of 16 rows, and the
+  // transposing V reads (4 rows x 4 pieces per 32 lanes).
+  static constexpr int kChunksPerRow = D / 8;                  // 16-byte pieces per row
+  static constexpr int kKElems = kBN * D;
+  static constexpr int kVElems = kBN * D;
   static constexpr int kSlotElems = kKElems + kVElems;
-  static constexpr int kChunksPerRow = D / 8;
-  static constexpr int kChunks = kBN * kChunksPerRow / kThreads;  // 16-byte pieces per thread per matrix
-  static constexpr int kRowsPerPass = kThreads / kChunksPerRow;
-  static_assert(kChunks >= 1 && kChunks * kThreads == kBN * kChunksPerRow, "tile must split evenly");
-  static_assert(kRowsPerPass % 16 == 0 && 16 % (64 / kChunksPerRow) == 0, "wave rows must share a block");
-  static_assert(kVUnits <= kThreads, "one V piece per thread at most");
+  static constexpr int kRowsPerLoad = 512 / D;                 // rows one 1 KiB load instruction fills
+  static constexpr int kLoads = kBN * D * 2 / 1024 / (kThreads / 64);  // load instructions per wave per matrix
+  static_assert(kLoads >= 1 && kLoads * (kThreads / 64) * 1024 == kBN * D * 2, "tile must split evenly");
+  static_assert(16 % kRowsPerLoad == 0, "a load instruction's rows must share a 16-key block");
+  // piece swizzle of row r (an involution-free bijection of the low bits)
+  static __device__ __forceinline__ int swz(int r) {
+    if constexpr (D == 128) return ((r & 3) << 2) | ((r >> 2) & 3);
+    else return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
+  }
+  static_assert(D == 64 || D == 128, "head dim 64 or 128");
 };
 
 struct PPParams {
@@ -102,11 +109,31 @@ struct PPParams {
   float* lse_acc;
 };
 
-// Column (LDS slot) of key `key` in a transposed V tile: within every 16
-// keys the groups of 4 are stored in the order 0,2,1,3 (bits 2 and 3
-// swapped), the order in which a lane's half of the S^T accumulator lists
-// them, so that a lane's 8 P values meet 8 contiguous V values.
-__device__ __forceinline__ int pp_v_slot(int key) { return (key & ~12) | ((key & 4) << 1) | ((key & 8) >> 1); }
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+// ds_read_b64_tr_b16: within each group of 16 lanes, source lane 4k+q names 4
+// consecutive bf16 of row k of a 4-row block; result lane 4q+t receives
+// column t of that lane quad's piece from rows 0..3, i.e. one column of the
+// block as 4 consecutive rows.
+__device__ __forceinline__ s16x4 lds_read_tr(const uint16_t* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(p));
+}
+
+// 16 bytes per lane from global memory straight into LDS: lane i writes
+// bytes [16 i, 16 i + 16) after lds_base (wave-uniform). Written as a
+// statement of its own rather than the compiler builtin: the compiler treats
+// every later LDS read as possibly aliasing such a load and waits for it to
+// complete, which would stall the matrix phase on the next slot's loads. The
+// statement has no output register (the data goes to LDS); the kernel waits
+// for these loads (vmcnt 0) itself before the barrier that publishes the
+// slot. Loads the compiler issues itself are counted in order with these, so
+// its own waits can only wait longer than needed, never shorter.
+__device__ __forceinline__ void lds_dma16(const void* src, const uint16_t* lds_base) {
+  const uint32_t m0v = __builtin_amdgcn_readfirstlane(
+      (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint16_t*)lds_base);
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(m0v) : "memory", "m0");
+}
+
 
 __device__ __forceinline__ float pp_max3(float a, float b, float c) { return fmaxf(a, fmaxf(b, c)); }
 
@@ -280,93 +307,61 @@ __global__ __launch_bounds__(kThreads, 1) void attn_pp_kernel(PPParams p) {
     for (int kk = 0; kk < D / 16; ++kk) qf[kk] = *(const bf16x8*)(src + 16 * kk);
   }
 
-  // ---- slot staging: piece i of a matrix covers row r_first + i*kRowsPerPass
-  const int c8 = tid % T::kChunksPerRow;
-  const int r_first = tid / T::kChunksPerRow;
+  // ---- slot staging: load instruction i of this wave fills tile rows
+  // ld_row(i) .. ld_row(i) + kRowsPerLoad - 1 of a matrix; this lane fetches
+  // the piece of row ld_row(i) + lane / kChunksPerRow that belongs at its
+  // place in the swizzled row
+  const int ld_rowbase = wave * T::kLoads * T::kRowsPerLoad + lane / T::kChunksPerRow;
+  auto ld_row = [&](int i) { return ld_rowbase + i * T::kRowsPerLoad; };
+  auto ld_piece = [&](int i) { return (lane % T::kChunksPerRow) ^ T::swz(ld_row(i)); };
+  auto ld_lds = [&](uint16_t* mat, int i) { return mat + (wave * T::kLoads + i) * 512; };  // wave-uniform
   const int64_t row_stride = (int64_t)p.hkv * D;
-  uint32_t off[T::kChunks];
-#pragma unroll
-  for (int i = 0; i < T::kChunks; ++i) {
-    const int r = r_first + i * T::kRowsPerPass;
-    if constexpr (PAGED) off[i] = (uint32_t)((r & 15) * D + c8 * 8);
-    else off[i] = (uint32_t)(r * row_stride + c8 * 8);
-  }
-  // paged: physical blocks of this thread's rows in the next slot's K tile
-  // and V tile, read from the block table one slot ahead of their loads
-  int pre_k[T::kChunks] = {};
-  int pre_v = 0;
-  auto load_k = [&](const TileRef& tr, u32x4* regs) {
-    const uint16_t* __restrict__ src = tr.k;
+  // paged: physical blocks of this wave's rows in the next slot's K tile and
+  // V tile (uniform over the wave: the rows of one load instruction never
+  // leave one 16-key block, clamped or not), read one slot ahead
+  int pre_k[T::kLoads] = {};
+  int pre_v[T::kLoads] = {};
+  // direct global->LDS loads of one matrix tile; rows past the visible range
+  // are clamped to its last row
+  auto load_mat = [&](const uint16_t* __restrict__ src, const TileRef& tr, const int* pre, uint16_t* mat) {
     const int j0 = tr.j0, n_end = tr.end;
-    const bool last = j0 + kBN > n_end;
-    if constexpr (PAGED) {
-      // physical blocks looked up one slot ahead (pre_k, uniform over the
-      // wave: its 4 rows of a piece never leave one 16-key block, clamped or
-      // not); rows past the visible range are clamped to its last row
-      const int64_t slab = (int64_t)p.hkv * 16 * D;
 #pragma unroll
-      for (int i = 0; i < T::kChunks; ++i) {
-        const int j = last ? min(j0 + r_first + i * T::kRowsPerPass, n_end - 1) : j0 + r_first + i * T::kRowsPerPass;
-        const uint16_t* base = src + (int64_t)pre_k[i] * slab + (int64_t)kvh * 16 * D;
-        regs[i] = *(const u32x4*)(base + (j & 15) * D + c8 * 8);
+    for (int i = 0; i < T::kLoads; ++i) {
+      const int j = min(j0 + ld_row(i), n_end - 1);
+      const uint16_t* g;
+      if constexpr (PAGED) {
+        g = src + ((int64_t)pre[i] * p.hkv + kvh) * 16 * D + (j & 15) * D + ld_piece(i) * 8;
+      } else {
+        g = src + (int64_t)j * row_stride + kvh * D + ld_piece(i) * 8;
       }
-    } else {
-      const uint16_t* b = src + ((int64_t)j0 * p.hkv + kvh) * D;
-#pragma unroll
-      for (int i = 0; i < T::kChunks; ++i) {
-        uint32_t o = off[i];
-        if (last) o = (uint32_t)(min(r_first + i * T::kRowsPerPass, n_end - 1 - j0) * row_stride + c8 * 8);
-        regs[i] = *(const u32x4*)(b + o);
-      }
+      lds_dma16(g, ld_lds(mat, i));
     }
   };
-  // V piece of thread tid < kVUnits: keys 2 kp, 2 kp + 1 of the tile, dims 8 dc .. 8 dc + 7
-  const int v_kp = tid % (kBN / 2), v_dc = tid / (kBN / 2);
   auto prefetch_tab = [&](int tk, int tv) {  // K tile tk, V tile tv
     if constexpr (PAGED) {
       const int* tab = p.block_table + (int64_t)seq * p.max_blocks;
       auto tab_at = [&](int b) { return tab_in_lds ? tab_sh[b] : tab[b]; };
-      if (tk < n) {
 #pragma unroll
-        for (int i = 0; i < T::kChunks; ++i)
-          pre_k[i] = __builtin_amdgcn_readfirstlane(
-              tab_at(min(tk * kBN + r_first + i * T::kRowsPerPass, seg0_end - 1) >> 4));
-      }
-      if (tv >= 0 && tv < n && tid < T::kVUnits) pre_v = tab_at(min(tv * kBN + 2 * v_kp, seg0_end - 1) >> 4);
-    }
-  };
-  auto load_v = [&](const TileRef& tr, u32x4* regs) {
-    if (tid >= T::kVUnits) return;
-    const uint16_t* __restrict__ vmat = tr.v;
-    const int j0 = tr.j0, n_end = tr.end;
-#pragma unroll
-    for (int r = 0; r < 2; ++r) {
-      const int j = min(j0 + 2 * v_kp + r, n_end - 1);
-      if constexpr (PAGED) {
-        // keys 2 kp and 2 kp + 1 (an even key and the next, or both clamped to
-        // the last visible key) lie in one 16-key block, looked up one slot
-        // ahead (pre_v)
-        regs[r] = *(const u32x4*)(vmat + ((int64_t)pre_v * p.hkv + kvh) * 16 * D + (j & 15) * D + v_dc * 8);
-      } else {
-        regs[r] = *(const u32x4*)(vmat + ((int64_t)j * p.hkv + kvh) * D + v_dc * 8);
+      for (int i = 0; i < T::kLoads; ++i) {
+        if (tk < n) pre_k[i] = __builtin_amdgcn_readfirstlane(tab_at(min(tk * kBN + ld_row(i), seg0_end - 1) >> 4));
+        if (tv >= 0 && tv < n)
+          pre_v[i] = __builtin_amdgcn_readfirstlane(tab_at(min(tv * kBN + ld_row(i), seg0_end - 1) >> 4));
       }
     }
   };
-  auto key_pos = [&](const TileRef& tr) -> int {  // position of key tid of the tile (tid < 64), INT_MAX past the end
-    const int j = tr.j0 + tid;
-    if (j >= tr.end) return INT_MAX;
+  // position of key tid of the tile (tid < 64): read (or derived) when the
+  // slot's loads are issued, finished when it is stored (INT_MAX past the
+  // end). The register is written only by the load itself, so issuing it
+  // never waits on the previous slot's read of the same register.
+  auto key_pos_issue = [&](const TileRef& tr) -> int {
+    const int j = min(tr.j0 + tid, tr.end - 1);
     if constexpr (PAGED) return rr_global_pos(j, p.cp, p.rank, p.il);
     else return p.causal ? tr.kp[j] : 0;
   };
+  int kp_j0 = 0, kp_end = 0;  // tile of the pending position read
   auto kslot = [&](int s) { return smem + s * T::kSlotElems; };
   auto vslot = [&](int s) { return smem + s * T::kSlotElems + T::kKElems; };
-  auto store_tile = [&](uint16_t* dst, int stride, const u32x4* regs) {
-#pragma unroll
-    for (int i = 0; i < T::kChunks; ++i)
-      *(u32x4*)(dst + (r_first + i * T::kRowsPerPass) * stride + c8 * 8) = regs[i];
-  };
 
-  u32x4 kreg[T::kChunks], vreg[2];
   int kp_reg = INT_MAX;
   // slot t = {K(t), V(t-1), positions of tile t}
   // slots are loaded for t = 0, 1, ..., n in order; the V of a slot is the
@@ -376,27 +371,32 @@ __global__ __launch_bounds__(kThreads, 1) void attn_pp_kernel(PPParams p) {
     TileRef tr{};
     if (t < n) {
       tr = tile_ref(t);
-      load_k(tr, kreg);
-      if (tid < kBN) kp_reg = key_pos(tr);
+      // positions first: any wait the compiler puts before reusing their
+      // register then precedes this slot's tile loads
+      if (tid < kBN) {
+        if constexpr (PAGED) {
+          kp_reg = key_pos_issue(tr);
+        } else if (p.causal) {
+          kp_reg = tr.kp[min(tr.j0 + tid, tr.end - 1)];
+        }
+        kp_j0 = tr.j0;
+        kp_end = tr.end;
+      }
+      load_mat(tr.k, tr, pre_k, kslot(t & 1));
     }
-    if (t >= 1) load_v(MERGED ? prev_tr : tile_ref(t - 1), vreg);
+    if (t >= 1) {
+      const TileRef vr = MERGED ? prev_tr : tile_ref(t - 1);
+      load_mat(vr.v, vr, pre_v, vslot(t & 1));
+    }
     prev_tr = tr;
   };
+  // the slot's tiles are in LDS once this wave's loads have completed (and,
+  // for the other waves, after the barrier that follows)
   auto store_slot = [&](int t) {
-    const int s = t & 1;
-    if (t < n) {
-      store_tile(kslot(s), T::kKStride, kreg);
-      if (tid < kBN) kpos_sh[s][tid] = kp_reg;
-    }
-    if (t >= 1 && tid < T::kVUnits) {
-      // transpose the key pair into 8 dim rows: one 4-byte (key, key+1) pair per row
-      uint16_t* vt = vslot(s) + (8 * v_dc) * T::kVStride + pp_v_slot(2 * v_kp);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const uint32_t w0 = vreg[0][e], w1 = vreg[1][e];
-        *(uint32_t*)(vt + (2 * e) * T::kVStride) = (w0 & 0xffffu) | (w1 << 16);
-        *(uint32_t*)(vt + (2 * e + 1) * T::kVStride) = (w0 >> 16) | (w1 & 0xffff0000u);
-      }
+    __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
+    if (t < n && tid < kBN) {
+      const int kp = PAGED || p.causal ? kp_reg : 0;
+      kpos_sh[t & 1][tid] = kp_j0 + tid >= kp_end ? INT_MAX : kp;
     }
     // paged: the blocks of the next slot (K(t+1), V(t)), read here at the end
     // of a phase, not on the way into the matrix work
@@ -413,8 +413,26 @@ __global__ __launch_bounds__(kThreads, 1) void attn_pp_kernel(PPParams p) {
   f32x16 s0 = {}, s1 = {};  // S(t) after phase A, P(t) in fp32 after phase B
   bool p_valid = false;     // s0/s1 hold P of the previous tile for this wave
 
-  const int k_lane = lr * T::kKStride + 8 * lc;
-  const int v_lane = lr * T::kVStride + 8 * lc;  // V^T rows (dims) lr (+32 db), slots 16 kst + 8 lc
+  // K operand k-step kk: row lr (+32 for the second key half), piece 2 kk + lc
+  int k_off[D / 16];
+#pragma unroll
+  for (int kk = 0; kk < D / 16; ++kk) k_off[kk] = lr * D + 8 * ((2 * kk + lc) ^ T::swz(lr));
+  // V^T operand (d-block db, k-step kst) from two transposing reads: within
+  // each 16 lanes, lane j16 names 4 bf16 of key row 4 lc + j16/4 (+8 for the
+  // second read, +16 kst), dims 32 db + 16 (g16 & 1) + 4 (j16 & 3); a lane
+  // receives 4 consecutive keys of dim 32 db + lr, which is the key order of
+  // its P values in the S^T accumulator
+  const int g16 = lane >> 4, j16 = lane & 15;
+  int v_off[D / 32][2];
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db) {
+#pragma unroll
+    for (int hi = 0; hi < 2; ++hi) {
+      const int r = 4 * lc + (j16 >> 2) + 8 * hi;
+      const int piece = 4 * db + 2 * (g16 & 1) + ((j16 >> 1) & 1);
+      v_off[db][hi] = r * D + 8 * (piece ^ T::swz(r)) + 4 * (j16 & 1);
+    }
+  }
 
   // A(t): O += V(t-1)^T P(t-1)^T, then S(t)^T = K(t) Q^T. The bf16 packing of
   // P(t-1) and its row sum run here, under the matrix work, to keep the
@@ -434,14 +452,17 @@ __global__ __launch_bounds__(kThreads, 1) void attn_pp_kernel(PPParams p) {
     const int s = t & 1;
     const bool do_pv = t >= 1 && p_valid;
     const bool do_qk = t < n && __builtin_amdgcn_readfirstlane(kpos_sh[s][0]) <= wave_qmax;
-    const uint16_t* vs = vslot(s) + v_lane;
-    const uint16_t* ks = kslot(s) + k_lane;
+    const uint16_t* vs = vslot(s);
+    const uint16_t* ks = kslot(s);
     constexpr int kPV = 4 * (D / 32), kQK = D / 8, kRing = 6;
     constexpr int kSumPer = (31 + kPV - 1) / kPV;  // row-sum adds per PV MFMA
     auto vop = [&](int i) {
-      return *(const bf16x8*)(vs + 32 * (i % (D / 32)) * T::kVStride + 16 * (i / (D / 32)));
+      const int db = i % (D / 32), kst = i / (D / 32);
+      const s16x4 lo = lds_read_tr(vs + 16 * kst * D + v_off[db][0]);
+      const s16x4 hi = lds_read_tr(vs + 16 * kst * D + v_off[db][1]);
+      return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
     };
-    auto kop = [&](int i) { return *(const bf16x8*)(ks + (i & 1) * 32 * T::kKStride + 16 * (i >> 1)); };
+    auto kop = [&](int i) { return *(const bf16x8*)(ks + (i & 1) * 32 * D + k_off[i >> 1]); };
     bf16x8 pb[4];
     float sums[31];  // [0, 16): s0[v] + s1[v]; node a >= 16: sums[2(a-16)] + sums[2(a-16)+1]
     auto pack_p = [&]() {
