@@ -178,7 +178,8 @@ cpa_status cpa_partial_attn(const void* q, const int32_t* q_pos, const int32_t* 
  * shards are already resident they can run as one launch. With causal masks
  * over zigzag shards the work of a query tile differs by an order of
  * magnitude between tiles and shards; given a workspace, a small pre-pass
- * orders the launch heaviest tile first, which keeps its tail short. Each
+ * orders the launch heaviest tile first, which keeps its tail short (it also
+ * records each tile's visible key-tile count there for the kernel). Each
  * shard's result is exactly what cpa_partial_attn returns for it, whatever
  * the order.
  *
