@@ -131,7 +131,13 @@ __device__ __forceinline__ s16x4 lds_read_tr(const uint16_t* p) {
 __device__ __forceinline__ void lds_dma16(const void* src, const uint16_t* lds_base) {
   const uint32_t m0v = __builtin_amdgcn_readfirstlane(
       (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint16_t*)lds_base);
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(m0v) : "memory", "m0");
+  // m0 is reserved to the compiler (a clobber of it is ignored), so the
+  // statement restores it
+  uint32_t saved;
+  asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %1, off\n\ts_mov_b32 m0, %0"
+               : "=&s"(saved)
+               : "v"(src), "s"(m0v)
+               : "memory");
 }
 
 

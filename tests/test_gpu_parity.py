@@ -187,6 +187,39 @@ def test_multi_shard_launch_equals_separate_calls(cpa, wl, harness, name, change
         assert_close(f64(run.o_parts[s]), f64(run.lse_parts[s]), o_ref, l_ref, f"multi {name} shard {s}", **tol)
 
 
+# many short sequences: 2000 and 2200 (shard, sequence) segments, 6000 and
+# 6600 units for the ordering pre-pass
+PREPASS = [
+    ("seqs_1000_cp2_r0", dict(batch=1000, len_range=(1, 700), lengths=(), cp=2, rank=0, hq=4, hkv=2, d=64)),
+    ("seqs_1100_cp2_r1", dict(batch=1100, len_range=(1, 700), lengths=(), cp=2, rank=1, hq=4, hkv=2, d=64)),
+]
+
+
+@pytest.mark.parametrize("name,changes", PREPASS, ids=[m[0] for m in PREPASS])
+def test_ordering_prepass_segments(cpa, wl, harness, name, changes):
+    """The launch order and per-unit key-tile counts from the pre-pass give
+    the bits of the separate per-step calls, which search the key positions
+    themselves."""
+    w = wl.scaled(wl.WORKLOADS["qwen2.5_3b_cp2_rank0"], name=name, seed=700 + len(name), **changes)
+    _say(f"case prepass {name}")
+    inp = harness.build(w, device="cuda")
+    assert inp["max_q"] <= 3 * 128, "the units must fit the pre-pass (8192)"
+    run = harness.Runner(inp)
+    assert run.workspace is not None
+    for i in range(w.cp):
+        run.partial(i)
+    torch.cuda.synchronize()
+    sep = [(o.clone(), l.clone()) for o, l in zip(run.o_parts, run.lse_parts)]
+    for o, l in zip(run.o_parts, run.lse_parts):
+        o.fill_(float("nan"))
+        l.fill_(float("nan"))
+    run.partials_batched(ordered=True)
+    torch.cuda.synchronize()
+    for s, (o, l) in enumerate(sep):
+        assert torch.equal(run.o_parts[s], o), f"{name} shard {s}: O differs from the separate call"
+        assert torch.equal(run.lse_parts[s], l), f"{name} shard {s}: LSE differs from the separate call"
+
+
 MERGED = [
     ("cp2_r0_ragged", dict(lengths=(300, 517, 1000), batch=3, len_range=(), cp=2, rank=0)),
     ("cp4_r2_d64_g4", dict(lengths=(777, 64, 2), batch=3, len_range=(), cp=4, rank=2, hq=8, hkv=2, d=64)),
