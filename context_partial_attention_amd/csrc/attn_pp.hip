@@ -13,10 +13,13 @@
 // one wave of each group. Work on KV tile t is split into two phases:
 //   A(t): O += V(t-1)^T P(t-1)^T and S(t)^T = K(t) Q^T   (matrix cores)
 //   B(t): mask, online softmax of S(t) -> P(t)           (vector ALUs)
-// Group 1 runs one phase behind group 0 and every phase ends with a
-// workgroup barrier, so on each SIMD one wave issues MFMAs while the other
-// does its softmax. Both groups see the same rows, hence the same masks and
-// tile counts, so neither waits on the other. The wave in phase A raises its
+// Group 1 runs one phase behind group 0, so on each SIMD one wave issues
+// MFMAs while the other does its softmax. A workgroup barrier ends every odd
+// phase (it publishes the next slot); between two barriers each group runs
+// one A and one B phase in opposite orders, which keeps the groups a phase
+// apart without a barrier in the middle (one there only added the waves'
+// skew). Both groups see the same rows, hence the same masks and tile
+// counts, so neither waits on the other. The wave in phase A raises its
 // issue priority: left to the hardware, the older wave (group 0) wins every
 // conflict and group 1's matrix work stalls behind group 0's softmax.
 //
@@ -163,7 +166,7 @@ template <int D, bool PAGED, bool OUT_BF16, bool MERGED>
 __global__ __launch_bounds__(kThreads, 1) void attn_pp_kernel(PPParams p) {
   using T = PPTile<D>;
   __shared__ __attribute__((aligned(16))) uint16_t smem[2 * T::kSlotElems];
-  __shared__ int kpos_sh[2][kBN];
+  __shared__ int kpos_sh[4][kBN];
 
   // ---- (sequence, query tile, KV head) group and head pair; the head pairs
   // of a group share an XCD, consecutive groups rotate over the 8 XCDs
@@ -402,7 +405,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_pp_kernel(PPParams p) {
     __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
     if (t < n && tid < kBN) {
       const int kp = PAGED || p.causal ? kp_reg : 0;
-      kpos_sh[t & 1][tid] = kp_j0 + tid >= kp_end ? INT_MAX : kp;
+      kpos_sh[t & 3][tid] = kp_j0 + tid >= kp_end ? INT_MAX : kp;
     }
     // paged: the blocks of the next slot (K(t+1), V(t)), read here at the end
     // of a phase, not on the way into the matrix work
@@ -457,7 +460,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_pp_kernel(PPParams p) {
     __builtin_amdgcn_s_setprio(2);
     const int s = t & 1;
     const bool do_pv = t >= 1 && p_valid;
-    const bool do_qk = t < n && __builtin_amdgcn_readfirstlane(kpos_sh[s][0]) <= wave_qmax;
+    const bool do_qk = t < n && __builtin_amdgcn_readfirstlane(kpos_sh[t & 3][0]) <= wave_qmax;
     const uint16_t* vs = vslot(s);
     const uint16_t* ks = kslot(s);
     constexpr int kPV = 4 * (D / 32), kQK = D / 8, kRing = 6;
@@ -543,7 +546,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_pp_kernel(PPParams p) {
   // B(t): mask and online softmax of S(t) -> P(t) (fp32, in place)
   auto phase_b = [&](int t) {
     __builtin_amdgcn_s_setprio(0);
-    const int* kp = kpos_sh[t & 1];
+    const int* kp = kpos_sh[t & 3];
     p_valid = __builtin_amdgcn_readfirstlane(kp[0]) <= wave_qmax;
     if (!p_valid) return;
     // accumulator element v of this lane holds key 8*(v/4) + 4*lc + v%4 (+32 for s1)
@@ -581,7 +584,11 @@ __global__ __launch_bounds__(kThreads, 1) void attn_pp_kernel(PPParams p) {
     store_slot(0);
     __syncthreads();
     // phases 0 .. 2n+1; group 0 runs A(t) in phase 2t and B(t) in 2t+1,
-    // group 1 one phase later; slot t+1 is loaded during phases 2t, 2t+1
+    // group 1 one phase later; slot t+1 is loaded during phases 2t, 2t+1.
+    // Only odd phases end in a barrier: a wave may then run a phase ahead of
+    // the other group, which is why the positions of a tile have four
+    // buffers (tile t's are read until phase 2t+2 and rewritten for tile t+4)
+    // while K and V need two (slot t+1's buffer is last read in phase 2t-1)
     for (int ph = 0; ph <= 2 * n + 1; ++ph) {
       const int t_ld = ph >> 1;
       if (!(ph & 1) && t_ld + 1 <= n) load_slot(t_ld + 1);
@@ -590,8 +597,10 @@ __global__ __launch_bounds__(kThreads, 1) void attn_pp_kernel(PPParams p) {
         if (!(q & 1)) phase_a(q >> 1);
         else phase_b(q >> 1);
       }
-      if ((ph & 1) && t_ld + 1 <= n) store_slot(t_ld + 1);
-      lds_barrier();
+      if (ph & 1) {
+        if (t_ld + 1 <= n) store_slot(t_ld + 1);
+        lds_barrier();
+      }
     }
   }
 
