@@ -22,6 +22,7 @@ import hashlib
 import json
 import os
 import platform
+import re
 import sys
 import time
 
@@ -258,11 +259,19 @@ def bench_workload(name: str, steps: int, warmup: int, next_rows: bool = True) -
 # ------------------------------------------------------------------ traffic from committed counters
 
 
+def _code_only(text: str) -> str:
+    """Source text without comments, trailing blanks or empty lines, so that a
+    comment edit does not mark the counters of an unchanged kernel stale."""
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    lines = (re.sub(r"//.*", "", ln).rstrip() for ln in text.splitlines())
+    return "\n".join(ln for ln in lines if ln)
+
+
 def _source_digest() -> str:
     h = hashlib.sha256()
     for f in ATTN_KERNEL_SOURCES:
-        with open(os.path.join(ROOT, "context_partial_attention_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, "context_partial_attention_amd", "csrc", f)) as fh:
+            h.update(_code_only(fh.read()).encode())
     return h.hexdigest()[:16]
 
 

@@ -75,7 +75,13 @@ struct PPTile {
   static constexpr int kLoads = kBN * D * 2 / 1024 / (kThreads / 64);  // load instructions per wave per matrix
   static_assert(kLoads >= 1 && kLoads * (kThreads / 64) * 1024 == kBN * D * 2, "tile must split evenly");
   static_assert(16 % kRowsPerLoad == 0, "a load instruction's rows must share a 16-key block");
-  // piece swizzle of row r (an involution-free bijection of the low bits)
+  // piece swizzle of row r. d = 128 (16 pieces, one row per 256-byte bank
+  // period): the low two row bits move to piece bits 2-3 and the next two to
+  // bits 0-1, a bijection on 16 consecutive rows (16 rows of one piece
+  // column land on 16 bank groups) that gives 4 consecutive rows distinct
+  // piece bits 2-3 (the 4 rows x 4 pieces of a transposing read). d = 64
+  // (8 pieces, two rows per bank period): row bit 1 to piece bit 2, row bits
+  // 2-3 to bits 0-1, so the 8 rows of each parity land on 8 groups.
   static __device__ __forceinline__ int swz(int r) {
     if constexpr (D == 128) return ((r & 3) << 2) | ((r >> 2) & 3);
     else return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);

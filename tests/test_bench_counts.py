@@ -103,3 +103,13 @@ def test_merge_bytes_formula(env):
     rows, parts = 1000 * w.hq, 2
     # each part: fp32 O (4 d bytes) and one fp32 LSE per row; out: bf16 O and fp32 LSE
     assert bench.merge_bytes(w, rows, parts, 2) == parts * rows * (4 * w.d + 4) + rows * (2 * w.d + 4)
+
+
+def test_source_digest_ignores_comments_only(env):
+    """The counter summaries stay valid across comment edits of the kernel
+    source, and go stale on any code change."""
+    bench = env[0]
+    src = "int a; // one\n/* two\n three */ int b;\n\n  // four\nint c;  \n"
+    assert bench._code_only(src) == "int a;\n int b;\nint c;"
+    assert bench._code_only(src.replace("// one", "// ONE")) == bench._code_only(src)
+    assert bench._code_only(src.replace("int c;", "int c = 1;")) != bench._code_only(src)
