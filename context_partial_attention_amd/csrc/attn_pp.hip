@@ -427,6 +427,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_pp_kernel(PPParams p) {
   constexpr float kTau = 8.f;  // lazy-rescale threshold (log2 units)
   f32x16 s0 = {}, s1 = {};  // S(t) after phase A, P(t) in fp32 after phase B
   bool p_valid = false;     // s0/s1 hold P of the previous tile for this wave
+  bool b_valid = false, b_mask = false;  // tile of the next B phase: any key visible / some masked
 
   // K operand k-step kk: row lr (+32 for the second key half), piece 2 kk + lc
   int k_off[D / 16];
@@ -460,13 +461,14 @@ __global__ __launch_bounds__(kThreads, 1) void attn_pp_kernel(PPParams p) {
   // ahead from a single register ring, so the first K reads are in flight
   // while the PV MFMAs run. The row sum of P is a pairwise tree whose adds
   // are spread over the PV MFMAs.
-  auto phase_a = [&](int t) {
+  auto phase_a_body = [&](int t) {
     // the wave feeding the matrix core issues first when both waves of a
     // SIMD have an instruction ready (by default the older wave would)
     __builtin_amdgcn_s_setprio(2);
     const int s = t & 1;
     const bool do_pv = t >= 1 && p_valid;
     const bool do_qk = t < n && __builtin_amdgcn_readfirstlane(kpos_sh[t & 3][0]) <= wave_qmax;
+    b_valid = do_qk;  // B(t) has work iff some key of tile t is visible to this wave
     const uint16_t* vs = vslot(s);
     const uint16_t* ks = kslot(s);
     constexpr int kPV = 4 * (D / 32), kQK = D / 8, kRing = 6;
@@ -549,14 +551,21 @@ __global__ __launch_bounds__(kThreads, 1) void attn_pp_kernel(PPParams p) {
     }
   };
 
+  // the flags B(t) needs, read here after the matrix work is issued rather
+  // than as the first (dependent) LDS reads of the softmax phase
+  auto phase_a = [&](int t) {
+    phase_a_body(t);
+    b_mask = b_valid && __builtin_amdgcn_readfirstlane(kpos_sh[t & 3][kBN - 1]) > wave_qmin;
+  };
+
   // B(t): mask and online softmax of S(t) -> P(t) (fp32, in place)
   auto phase_b = [&](int t) {
     __builtin_amdgcn_s_setprio(0);
     const int* kp = kpos_sh[t & 3];
-    p_valid = __builtin_amdgcn_readfirstlane(kp[0]) <= wave_qmax;
+    p_valid = b_valid;
     if (!p_valid) return;
     // accumulator element v of this lane holds key 8*(v/4) + 4*lc + v%4 (+32 for s1)
-    if (__builtin_amdgcn_readfirstlane(kp[kBN - 1]) > wave_qmin) {
+    if (b_mask) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
         const int key = 8 * (v >> 2) + 4 * lc + (v & 3);
