@@ -150,6 +150,21 @@ __device__ __forceinline__ void lds_dma16(const void* src, const uint16_t* lds_b
 }
 
 
+// Value of the lane 32 apart (lane ^ 32), combined: v_permlane32_swap
+// exchanges the upper half of one register with the lower half of another;
+// with both operands x, each lane ends with x and its partner's x, one in
+// each result, so a symmetric combination needs no lane test. A VALU swap
+// rather than an LDS permute, which would queue behind the other wave's
+// operand reads.
+__device__ __forceinline__ float pp_half_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float pp_half_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 __device__ __forceinline__ float pp_max3(float a, float b, float c) { return fmaxf(a, fmaxf(b, c)); }
 
 // Entries of the ascending array a[0..n) that are <= x (whole workgroup).
@@ -576,7 +591,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_pp_kernel(PPParams p) {
     float mx = fmaxf(s0[0], s1[0]);
 #pragma unroll
     for (int v = 1; v < 16; ++v) mx = pp_max3(mx, s0[v], s1[v]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * sl2;
+    mx = pp_half_max(mx) * sl2;
     if (__ballot(mx > m_run + kTau) != 0) {
       const float m_new = fmaxf(m_run, mx);
       const float alpha = (m_new == kNegInf) ? 1.f : hw_exp2(m_run - m_new);
@@ -620,7 +635,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_pp_kernel(PPParams p) {
   }
 
   // ---- epilogue
-  const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
+  const float l_tot = pp_half_sum(l_run);
   if (!row_ok) return;
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
   const int64_t obase = ((int64_t)my_row * p.hq + h) * D;
