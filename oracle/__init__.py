@@ -18,4 +18,5 @@ from .cpattn_oracle import (  # noqa: F401
     lse_merge,
     visible_pairs,
     choose_pass,
+    pass_cost,
 )

@@ -328,3 +328,56 @@ def choose_pass(q_lens, kv_lens, hq: int, hkv: int, d: int, elem_bytes: int = 2)
     kv_bytes = 2 * hkv * d * elem_bytes * t_kv
     q_bytes = hq * d * elem_bytes * t_q
     return {"pass_kv": kv_bytes < q_bytes, "kv_bytes": kv_bytes, "q_bytes": q_bytes}
+
+
+def pass_cost(q_lens, kv_lens, hq: int, hkv: int, d: int, elem_bytes: int, cp: int,
+              link_bytes_per_s: float, mfma_flops_per_s: float) -> dict:
+    """Per-step cost of the two exchange schemes for a prefill batch.
+
+    [PASSKV], Purpose: the exchanged shard is chosen from the relative sizes
+    of Q and KV, and the partial-attention compute of a step is what hides
+    the transfer of the next shard. Readings taken:
+      * a rank's work is 1/cp of the batch's (zigzag and round-robin shards
+        balance it) and a step is 1/cp of a rank's work, so a step computes
+        4 * d * hq * pairs / cp^2 FLOP, where pairs counts the (new token,
+        context key) pairs the causal mask lets through: new token i of a
+        sequence with c cached tokens sits at position c + i and sees c + i + 1
+        keys;
+      * a step moves one rank's shard over one link: K+V of T_kv / cp context
+        tokens under pass-KV, Q of T_q / cp new tokens under pass-Q;
+      * a transfer is hidden when it takes no longer than the step's compute
+        at the given MFMA rate.
+    The choice itself is `choose_pass` (fewer bytes moved). q_lens: new tokens
+    per sequence; kv_lens: context tokens per sequence (cached + new).
+    """
+    if cp < 1 or link_bytes_per_s <= 0 or mfma_flops_per_s <= 0:
+        raise ValueError("need cp >= 1 and positive rates")
+    choice = choose_pass(q_lens, kv_lens, hq, hkv, d, elem_bytes)
+    pairs = 0
+    for ql, kl in zip(q_lens, kv_lens):
+        ql, kl = int(ql), int(kl)
+        if ql > kl:
+            raise ValueError("a sequence has more new tokens than context tokens")
+        cached = kl - ql
+        for i in range(ql):  # one new token at a time
+            pairs += cached + i + 1
+    step_flops = 4 * d * hq * pairs / (cp * cp)
+    kv_step = choice["kv_bytes"] / cp
+    q_step = choice["q_bytes"] / cp
+    t_compute = step_flops / mfma_flops_per_s
+    t_kv = kv_step / link_bytes_per_s
+    t_q = q_step / link_bytes_per_s
+    return {
+        "pass_kv": choice["pass_kv"],
+        "kv_bytes": choice["kv_bytes"],
+        "q_bytes": choice["q_bytes"],
+        "pairs": pairs,
+        "kv_step_bytes": kv_step,
+        "q_step_bytes": q_step,
+        "step_flops": step_flops,
+        "kv_transfer_s": t_kv,
+        "q_transfer_s": t_q,
+        "step_compute_s": t_compute,
+        "kv_hidden": t_kv <= t_compute,
+        "q_hidden": t_q <= t_compute,
+    }
