@@ -25,5 +25,6 @@ from .binding import (  # noqa: F401
     partial_attn_multi_workspace,
     partial_attn_paged,
     partial_attn_paged_workspace,
+    pass_cost,
     rr_placement,
 )

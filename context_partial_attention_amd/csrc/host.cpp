@@ -164,3 +164,43 @@ extern "C" cpa_status cpa_choose_pass(int32_t num_seqs, const int32_t* q_lens, c
   if (q_bytes) *q_bytes = (int64_t)qb;
   return CPA_OK;
 }
+
+// Per-step cost of the two schemes: a step moves one rank's shard (1/cp of the
+// byte totals) and computes 1/cp^2 of the batch's causal pairs.
+extern "C" cpa_status cpa_pass_cost(int32_t num_seqs, const int32_t* q_lens, const int32_t* kv_lens, int32_t hq,
+                                    int32_t hkv, int32_t d, int32_t elem_bytes, int32_t cp_size,
+                                    double link_bytes_per_s, double mfma_flops_per_s, cpa_pass_cost_t* out) {
+  const char* fn = "cpa_pass_cost";
+  if (!out) return fail(CPA_ERR_INVALID_ARG, "%s: out is NULL", fn);
+  if (cp_size < 1) return fail(CPA_ERR_INVALID_ARG, "%s: cp_size %d < 1", fn, cp_size);
+  auto good_rate = [](double r) { return r > 0.0 && r <= 1.7e308; };  // also false for NaN
+  if (!good_rate(link_bytes_per_s) || !good_rate(mfma_flops_per_s))
+    return fail(CPA_ERR_INVALID_ARG, "%s: rates must be positive and finite", fn);
+  int32_t pass_kv = 0;
+  int64_t kvb = 0, qb = 0;
+  cpa_status st = cpa_choose_pass(num_seqs, q_lens, kv_lens, hq, hkv, d, elem_bytes, &pass_kv, &kvb, &qb);
+  if (st != CPA_OK) return st;
+  __int128 pairs = 0;
+  for (int32_t b = 0; b < num_seqs; ++b) {
+    const int64_t ql = q_lens[b], kl = kv_lens[b];
+    if (ql > kl) return fail(CPA_ERR_INVALID_ARG, "%s: q_lens[%d] > kv_lens[%d]", fn, b, b);
+    // new token i sees (kl - ql) + i + 1 keys: sum over i < ql
+    pairs += (__int128)ql * (kl - ql) + (__int128)ql * (ql + 1) / 2;
+  }
+  const __int128 flops = pairs * 4 * d * hq;
+  if (flops > (__int128)INT64_MAX) return fail(CPA_ERR_INVALID_ARG, "%s: pair count overflows", fn);
+  const double cp = (double)cp_size;
+  out->pass_kv = pass_kv;
+  out->kv_bytes = kvb;
+  out->q_bytes = qb;
+  out->pairs = (int64_t)pairs;
+  out->kv_step_bytes = (double)kvb / cp;
+  out->q_step_bytes = (double)qb / cp;
+  out->step_flops = (double)(int64_t)flops / (cp * cp);
+  out->kv_transfer_s = out->kv_step_bytes / link_bytes_per_s;
+  out->q_transfer_s = out->q_step_bytes / link_bytes_per_s;
+  out->step_compute_s = out->step_flops / mfma_flops_per_s;
+  out->kv_hidden = out->kv_transfer_s <= out->step_compute_s ? 1 : 0;
+  out->q_hidden = out->q_transfer_s <= out->step_compute_s ? 1 : 0;
+  return CPA_OK;
+}

@@ -155,6 +155,16 @@ class Runner:
             if need:
                 self.workspace = torch.empty(need, dtype=torch.uint8, device=dev)
 
+    def outputs(self) -> list:
+        """Every output buffer of the step (partials, merged O and LSE)."""
+        return [self.o, self.lse] + self.o_parts + self.lse_parts
+
+    def poison(self):
+        """Fills every output with NaN, so that a row no kernel writes shows up
+        as NaN in the results."""
+        for t in self.outputs():
+            t.fill_(float("nan"))
+
     def partial(self, i: int, stream=None):
         """Partial i of the schedule (pass-KV step i, or rank i's paged shard)."""
         inp, w = self.inp, self.w

@@ -139,6 +139,48 @@ cpa_status cpa_choose_pass(int32_t num_seqs, const int32_t* q_lens, const int32_
                            int32_t* pass_kv, int64_t* kv_bytes, int64_t* q_bytes);
 
 /* ---------------------------------------------------------------------------
+ * cpa_pass_cost — per-step transfer and compute of the two exchange schemes
+ * for a prefill batch (host).
+ *
+ * [PASSKV], Purpose: the shard to exchange follows the relative sizes of Q
+ * and KV, and the partial attention of a step is the compute that hides the
+ * transfer of the next shard. A rank's work is 1/cp of the batch's (the
+ * zigzag and round-robin shards balance it) and one step is 1/cp of a rank's
+ * work: step_flops = 4*d*hq*pairs / cp^2, where pairs counts the (new token,
+ * context key) pairs of the causal mask (new token i of a sequence with c
+ * cached tokens sees c + i + 1 keys). A step moves one rank's shard over one
+ * link: kv_bytes / cp under pass-KV, q_bytes / cp under pass-Q (the byte
+ * totals of cpa_choose_pass). A transfer is hidden when it takes no longer
+ * than the step's compute at mfma_flops_per_s.
+ *
+ * In:  as cpa_choose_pass, plus cp_size >= 1 and the two rates (> 0, finite):
+ *      link_bytes_per_s (one link, e.g. ~153e9 for one xGMI link) and
+ *      mfma_flops_per_s (the partial-attention rate the caller achieves).
+ *      q_lens[b] <= kv_lens[b].
+ * Out: *out (required), every field written.
+ * Errors: CPA_ERR_INVALID_ARG as cpa_choose_pass, and for cp_size < 1, a rate
+ *      that is not a positive finite number, or q_lens[b] > kv_lens[b].
+ * ------------------------------------------------------------------------- */
+typedef struct {
+  int32_t pass_kv;       /* the choice of cpa_choose_pass */
+  int32_t kv_hidden;     /* pass-KV: a step's KV transfer fits under its compute */
+  int32_t q_hidden;      /* pass-Q: a step's Q transfer fits under its compute */
+  int64_t kv_bytes;      /* K+V bytes of the batch's context */
+  int64_t q_bytes;       /* Q bytes of the batch's new tokens */
+  int64_t pairs;         /* causal (new token, context key) pairs of the batch */
+  double kv_step_bytes;  /* kv_bytes / cp */
+  double q_step_bytes;   /* q_bytes / cp */
+  double step_flops;     /* 4*d*hq*pairs / cp^2 */
+  double kv_transfer_s;  /* kv_step_bytes / link_bytes_per_s */
+  double q_transfer_s;   /* q_step_bytes / link_bytes_per_s */
+  double step_compute_s; /* step_flops / mfma_flops_per_s */
+} cpa_pass_cost_t;
+
+cpa_status cpa_pass_cost(int32_t num_seqs, const int32_t* q_lens, const int32_t* kv_lens, int32_t hq,
+                         int32_t hkv, int32_t d, int32_t elem_bytes, int32_t cp_size,
+                         double link_bytes_per_s, double mfma_flops_per_s, cpa_pass_cost_t* out);
+
+/* ---------------------------------------------------------------------------
  * cpa_partial_attn — one pass-KV step: a packed Q shard against one packed,
  * contiguous KV shard, giving partial O and LSE (device).
  *

@@ -233,3 +233,41 @@ def test_accumulate_call_validation_before_gpu(cpa):
     assert acc(hkv=3) == -1  # hq not a multiple of hkv
     assert acc(hkv=8) == -2  # GQA group of 1: not supported
     assert acc(dt=1) == -2  # fp32 inputs: not supported
+
+
+def test_pass_cost_matches_oracle(cpa):
+    """cpa_pass_cost against oracle.pass_cost: integers and flags bit-exact,
+    the per-step figures to the last bit of a double (both sides compute the
+    same correctly rounded quotients of exact integers)."""
+    rng = np.random.default_rng(11)
+    cases = [([131072], [131072], 32, 8, 128, 2, 4), ([4096, 4096], [69632, 69632], 16, 2, 128, 2, 4),
+             ([1], [1], 8, 2, 64, 2, 2), ([0, 0], [5, 0], 4, 4, 64, 1, 3)]
+    for _ in range(20):
+        n = int(rng.integers(1, 5))
+        kv = rng.integers(0, 20000, size=n)
+        q = np.minimum(kv, rng.integers(0, 5000, size=n))
+        g = int(rng.choice([1, 2, 4, 8]))
+        hkv = int(rng.choice([1, 2, 8]))
+        cases.append((q.tolist(), kv.tolist(), g * hkv, hkv, int(rng.choice([64, 128])), int(rng.choice([1, 2])),
+                      int(rng.integers(1, 9))))
+    for q, kv, hq, hkv, d, eb, cp in cases:
+        for link, mfma in ((1.53e11, 1.25e15), (1e9, 1e12), (3e11, 7e14)):
+            got = cpa.pass_cost(q, kv, hq, hkv, d, eb, cp, link, mfma)
+            want = oracle.pass_cost(q, kv, hq, hkv, d, eb, cp, link, mfma)
+            for key, val in want.items():
+                assert got[key] == val, (key, got[key], val, q, kv, hq, hkv, d, eb, cp)
+
+
+def test_pass_cost_errors(cpa):
+    lib = cpa.load_library()
+    r = cpa.binding.PassCost()
+    lens = (ctypes.c_int32 * 1)(5)
+    small = (ctypes.c_int32 * 1)(4)
+    assert lib.cpa_pass_cost(1, lens, lens, 8, 2, 64, 2, 2, 1e11, 1e15, None) == -1  # NULL out
+    assert lib.cpa_pass_cost(1, lens, lens, 8, 2, 64, 2, 0, 1e11, 1e15, ctypes.byref(r)) == -1  # cp 0
+    assert lib.cpa_pass_cost(1, lens, lens, 8, 2, 64, 2, 2, 0.0, 1e15, ctypes.byref(r)) == -1  # zero rate
+    assert lib.cpa_pass_cost(1, lens, lens, 8, 2, 64, 2, 2, float("nan"), 1e15, ctypes.byref(r)) == -1
+    assert lib.cpa_pass_cost(1, lens, lens, 8, 2, 64, 2, 2, 1e11, float("inf"), ctypes.byref(r)) == -1
+    assert lib.cpa_pass_cost(1, lens, small, 8, 2, 64, 2, 2, 1e11, 1e15, ctypes.byref(r)) == -1  # q > kv
+    assert lib.cpa_pass_cost(1, lens, lens, 8, 2, 64, 2, 2, 1e11, 1e15, ctypes.byref(r)) == 0
+    assert r.pairs == 15
