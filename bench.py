@@ -7,8 +7,9 @@ rank computes, then the merge of all partials (other ranks' partials already
 resident in HBM where the schedule has them). Inputs are seeded synthetic
 tensors resident in HBM before timing starts.
 
-Headline (`value`): the Qwen2.5-3B-shaped cp=2 rank-0 pass-KV workload
-(4 sequences of 2048..8192 tokens, 16/2 heads, d=128, bf16): algorithmic
+Headline (`value`): the largest workload, the Llama-3-8B-shaped 128K-token
+cp=4 rank-1 pass-KV share (1 sequence of 131072 tokens, zigzag into 8 chunks,
+32/8 heads, d=128, bf16; 4 partial attentions + 4-way merge): algorithmic
 TFLOP/s = 4 * d * hq * (visible causal pairs) / step time. The other
 full-size workloads are reported under "workloads" (TFLOP/s for prefill,
 GB/s for decode and for every merge).
@@ -32,13 +33,13 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "partial-attn+merge TFLOP/s and % bf16 MFMA peak (prefill); GB/s (decode)"
-HEADLINE = "qwen2.5_3b_cp2_rank0"
-DEFAULT_WORKLOADS = [HEADLINE, "llama3_8b_128k_cp4_rank1", "chunked_prefill_passq_cp4", "allgather_decode_cp2"]
+HEADLINE = "llama3_8b_128k_cp4_rank1"
+DEFAULT_WORKLOADS = [HEADLINE, "qwen2.5_3b_cp2_rank0", "chunked_prefill_passq_cp4", "allgather_decode_cp2"]
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0  # MI355X HBM3E
 # dominant kernel of the headline step and the committed counter summary of it
 ATTN_KERNEL_SOURCES = ("attn_pp.hip", "device_common.h")
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_pp_qwen2.5_3b_cp2_traffic.md")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_pp_llama3_8b_128k_traffic.md")
 
 
 def log(msg: str):
@@ -298,10 +299,13 @@ def committed_traffic():
 # ------------------------------------------------------------------ CPU baseline (oracle)
 
 
-def cpu_baseline(name: str, budget_s: float = 10.0) -> dict:
-    """Times the oracle on the host on the headline workload: whole sequences
-    (rank 0's shard, all heads, both pass-KV steps and the merge), added one
-    by one, and the whole set repeated, until about `budget_s` of CPU work."""
+def cpu_baseline(name: str, budget_s: float = 15.0, block_rows: int = 64) -> dict:
+    """Times the oracle on the host on a bounded sample of a pass-KV workload:
+    blocks of `block_rows` consecutive query rows of the rank's zigzag shard,
+    taken at evenly spread offsets through the shard (cheap early rows and
+    expensive late ones alike), each with all heads against every step's KV
+    shard plus the merge, until about `budget_s` of CPU work. The rate counts
+    the algorithmic FLOPs (visible pairs) of the rows done."""
     import torch
     from threadpoolctl import threadpool_info
 
@@ -310,38 +314,52 @@ def cpu_baseline(name: str, budget_s: float = 10.0) -> dict:
 
     w = WORKLOADS[name]
     lens = seq_lengths(w)
-    data = [tuple(t.float().numpy().astype(np.float64) for t in draw_sequence(w, b, L, L, device="cpu"))
-            for b, L in enumerate(lens)]
-    done_flops, elapsed, used, passes = 0, 0.0, 0, 0
-    while elapsed < budget_s:
-        for b, L in enumerate(lens):
-            q, k, v = data[b]
-            t0 = time.perf_counter()
-            mine = oracle.zigzag_partition([L], w.cp, w.rank)
-            qp = mine["positions"]
-            parts, kps = [], []
+    mine = oracle.zigzag_partition(lens, w.cp, w.rank)
+    cu, qpos_all, src_all = mine["cu_seqlens"], mine["positions"], mine["src_index"]
+    n_rows = int(cu[-1])
+    starts = [int(x) for x in np.linspace(0, max(0, n_rows - block_rows), 16).round()]
+    # shard tensors of every sequence, fp64 on the host (values drawn on the CPU:
+    # the timing does not depend on them)
+    data = {}
+    def seq_data(b):
+        if b not in data:
+            L = lens[b]
+            q, k, v = draw_sequence(w, b, L, L, device="cpu")
+            steps = []
             for s in range(w.cp):
-                src = oracle.zigzag_partition([L], w.cp, (w.rank - s) % w.cp)
-                kp = src["positions"]
-                kps.append(kp)
-                parts.append(oracle.partial_attn(q[qp], qp, [0, len(qp)], k[kp], v[kp], kp, [0, len(kp)], w.scale))
-            oracle.lse_merge([p[0] for p in parts], [p[1] for p in parts])
-            elapsed += time.perf_counter() - t0
-            done_flops += 4 * w.d * w.hq * sum(int(np.searchsorted(kp, qp, side="right").sum()) for kp in kps)
-            used = max(used, b + 1)
-            if elapsed >= budget_s:
-                break
-        passes += 1
-    del torch
+                part = oracle.zigzag_partition([L], w.cp, (w.rank - s) % w.cp)
+                kp = part["positions"]
+                steps.append((k[kp].float().numpy().astype(np.float64), v[kp].float().numpy().astype(np.float64),
+                              kp))
+            data[b] = (q, steps)
+        return data[b]
+
+    done_flops, elapsed, blocks = 0, 0.0, 0
+    for a in starts:
+        b = int(np.searchsorted(cu, a, side="right") - 1)
+        e = min(a + block_rows, int(cu[b + 1]))
+        q_seq, steps = seq_data(b)
+        qp = qpos_all[a:e]
+        qb = q_seq[torch.as_tensor(qp)].float().numpy().astype(np.float64)
+        t0 = time.perf_counter()
+        parts = [oracle.partial_attn(qb, qp, [0, e - a], k, v, kp, [0, len(kp)], w.scale) for k, v, kp in steps]
+        oracle.lse_merge([p[0] for p in parts], [p[1] for p in parts])
+        elapsed += time.perf_counter() - t0
+        done_flops += 4 * w.d * w.hq * sum(int(np.searchsorted(kp, qp, side="right").sum()) for _, _, kp in steps)
+        blocks += 1
+        if elapsed >= budget_s:
+            break
+    del src_all, torch
     threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     return {
         "value": done_flops / elapsed / 1e12,
         "unit": "TFLOP/s",
         "cores": int(threads),
         "kind": "oracle",
-        "sample": f"the whole workload: sequences of lengths {lens}, rank {w.rank}'s zigzag shard, all {w.hq} heads, "
-                  f"{w.cp} pass-KV steps + merge, fp64 NumPy, repeated ({passes} pass(es), the last partial) for "
-                  f"{elapsed:.1f} s",
+        "sample": f"{blocks} blocks of {block_rows} consecutive query rows at evenly spread offsets of rank "
+                  f"{w.rank}'s zigzag shard of the {name} workload (sequence lengths {lens}), all {w.hq} heads, "
+                  f"against all {w.cp} pass-KV steps' KV shards, plus the merge; fp64 NumPy; "
+                  f"{done_flops / 1e9:.1f} GFLOP of visible pairs in {elapsed:.1f} s",
         "seconds": elapsed,
         "cpu": platform.processor() or platform.machine(),
     }
@@ -426,6 +444,9 @@ def main():
         results[name] = bench_workload(name, args.steps, args.warmup, next_rows=not args.no_next_rows)
         log(f"[bench] {name}: {json.dumps({k: v for k, v in results[name].items() if k != 'description'})}")
     h = results[HEADLINE]
+    from context_partial_attention_amd.workloads import WORKLOADS
+
+    hw = WORKLOADS[HEADLINE]
     # dominant kernel of the headline: the batched partial-attention launch
     part_ms = float(np.mean(h["partial_ms"]))
     flops_per_launch = h["flops_per_step"] / len(h["partial_ms"])
@@ -448,17 +469,17 @@ def main():
         "config": {
             "workload": HEADLINE,
             "seq_lens": h["seq_lens"],
-            "cp": 2,
-            "rank": 0,
-            "hq": 16,
-            "hkv": 2,
-            "d": 128,
-            "step": "2 pass-KV partial attentions (one batched launch) + 2-way LSE merge (bf16 out); "
+            "cp": hw.cp,
+            "rank": hw.rank,
+            "hq": hw.hq,
+            "hkv": hw.hkv,
+            "d": hw.d,
+            "step": f"{hw.cp} pass-KV partial attentions (one batched launch) + {hw.cp}-way LSE merge (bf16 out); "
                     f"the timed loop replays a captured HIP graph of {h['steps_per_graph']} consecutive steps",
         },
         "roofline": {
-            "kernel": "attn_pp_kernel<128, contiguous, fp32 out, partials>, both pass-KV steps in one launch "
-                      "(event time includes its launch-order pre-pass)",
+            "kernel": f"attn_pp_kernel<{hw.d}, contiguous, fp32 out, partials>, all {hw.cp} pass-KV steps in one "
+                      "launch (event time includes its launch-order pre-pass)",
             "bound": "mfma",
             "achieved": achieved,
             "peak": PEAK_BF16_TFLOPS,

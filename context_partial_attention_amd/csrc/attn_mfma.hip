@@ -23,9 +23,9 @@
 //    the order in which the S^T accumulator lists a lane's keys.
 //  * With RB = 2 every K and V operand read from LDS would feed two MFMAs (one
 //    per 32-row block), halving LDS traffic per FLOP; the wave then holds ~400
-//    registers and runs alone on its SIMD. That variant is compiled but not
-//    selected (kUseTwoRowBlocks): it measured slower than RB = 1, two 32-row
-//    waves per SIMD.
+//    registers and runs alone on its SIMD, with no room left to compute the
+//    next tile's S during the softmax. Written that way it measured slower
+//    than RB = 1 (two 32-row waves per SIMD), so only RB = 1 is built.
 // The two-group kernel (attn_pp.hip) serves every even GQA group; this one
 // serves odd groups.
 //  * K and V tiles of 64 keys are double-buffered in LDS, K one tile ahead of
@@ -59,9 +59,6 @@ namespace cpa {
 namespace {
 
 constexpr int kBN = 64;   // keys per main-loop step
-// 64-row waves (one per SIMD) are slower than 32-row waves two per SIMD
-// without an explicit MFMA/VALU overlap scheme, so they are not selected.
-constexpr bool kUseTwoRowBlocks = false;
 constexpr int kThreads = 256;
 
 template <int D>
@@ -528,19 +525,15 @@ cpa_status launch_attn_mfma(const AttnArgs& a, bool paged, hipStream_t st) {
   p.causal = a.causal;
   p.o = a.o;
   p.lse = a.lse;
-  // 256-row workgroups (one wave per SIMD, half the LDS traffic per FLOP) when
-  // they still give every CU several workgroups; 128-row ones otherwise.
-  const int64_t big_groups = cdiv(a.max_q, 256) * a.num_seqs * a.hkv;
-  const int rb = (big_groups * p.g >= 4 * 256 && kUseTwoRowBlocks) ? 2 : 1;
-  const int64_t n_qtiles = cdiv(a.max_q, 128 * rb);
+  const int64_t n_qtiles = cdiv(a.max_q, 128);
   const int64_t n_groups = n_qtiles * a.num_seqs * a.hkv;
   const int64_t blocks = cdiv(n_groups, 8) * 8 * p.g;
   if (blocks > INT32_MAX) return fail(CPA_ERR_INVALID_ARG, "cpa_partial_attn: problem too large for one launch");
   p.n_groups = (int)n_groups;
   if (blocks == 0) return CPA_OK;
   const uint32_t nb = (uint32_t)blocks;
-  if (a.d == 64) rb == 2 ? launch_d<64, 2>(p, nb, paged, a.o_bf16, st) : launch_d<64, 1>(p, nb, paged, a.o_bf16, st);
-  else rb == 2 ? launch_d<128, 2>(p, nb, paged, a.o_bf16, st) : launch_d<128, 1>(p, nb, paged, a.o_bf16, st);
+  if (a.d == 64) launch_d<64, 1>(p, nb, paged, a.o_bf16, st);
+  else launch_d<128, 1>(p, nb, paged, a.o_bf16, st);
   return check_launch(paged ? "cpa_partial_attn_paged (prefill)" : "cpa_partial_attn (bf16)");
 }
 

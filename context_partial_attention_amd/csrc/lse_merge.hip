@@ -6,8 +6,9 @@
 // Purpose).
 //
 // HBM-bound: every byte of every partial is read once and the result written
-// once. One thread owns 8 consecutive elements of a row, issues all of its
-// loads before any arithmetic, and the LSE arithmetic is done in base 2 on
+// once. One thread owns two groups of 4 elements of a row, half a row apart,
+// issues all of its loads before any arithmetic, and the LSE arithmetic is
+// done in base 2 on
 // v_exp_f32 / v_log_f32. Two and four parts (the common CP sizes) have their
 // own instantiations so the registers are sized for them.
 #include "cpa_internal.h"
