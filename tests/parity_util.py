@@ -48,6 +48,7 @@ def expected_pass_kv(inp: dict, rows=None):
         k = f64(k_all.index_select(0, kidx))
         v = f64(v_all.index_select(0, kidx))
         parts.append(oracle.partial_attn(q_sel, qpos, cu_sel, k, v, kp["positions"], kp["cu_seqlens"], w.scale))
+        print(f"    oracle: step {s} done ({len(rows)} rows)", flush=True)
     merged = oracle.lse_merge([p[0] for p in parts], [p[1] for p in parts])
     return rows, parts, merged
 
@@ -62,7 +63,9 @@ def expected_round_robin(inp: dict, rows=None):
     seq_of_row = np.searchsorted(cu, rows, side="right") - 1
     parts_o = [np.zeros((len(rows), w.hq, w.d)) for _ in range(w.cp)]
     parts_l = [np.zeros((len(rows), w.hq)) for _ in range(w.cp)]
-    for b in np.unique(seq_of_row):
+    for i, b in enumerate(np.unique(seq_of_row)):
+        if i % 32 == 31:
+            print(f"    oracle: {i + 1} sequences done", flush=True)
         sel = np.nonzero(seq_of_row == b)[0]
         local_rows = rows[sel] - cu[b]
         L = lens[b]
