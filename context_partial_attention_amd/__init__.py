@@ -22,6 +22,7 @@ from .binding import (  # noqa: F401
     partial_attn_accumulate,
     partial_attn_merged,
     partial_attn_multi,
+    partial_attn_multi_noalloc,
     partial_attn_multi_workspace,
     partial_attn_paged,
     partial_attn_paged_workspace,

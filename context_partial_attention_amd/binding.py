@@ -79,6 +79,11 @@ def load_library():
                                            ctypes.POINTER(_p), ctypes.POINTER(_p), _i32, _i32, _i32, _i32, _i32,
                                            _i32, _f32, _i32, ctypes.POINTER(_p), _i32, ctypes.POINTER(_p), _p,
                                            ctypes.c_size_t, _p]
+    lib.cpa_partial_attn_multi_noalloc.restype = _i32
+    lib.cpa_partial_attn_multi_noalloc.argtypes = [_i32, _p, _p, _p, ctypes.POINTER(_p), ctypes.POINTER(_p),
+                                                   ctypes.POINTER(_p), ctypes.POINTER(_p), _i32, _i32, _i32, _i32,
+                                                   _i32, _i32, _f32, _i32, ctypes.POINTER(_p), _i32,
+                                                   ctypes.POINTER(_p), _p]
     lib.cpa_partial_attn_merged.restype = _i32
     lib.cpa_partial_attn_merged.argtypes = [_i32, _p, _p, _p, ctypes.POINTER(_p), ctypes.POINTER(_p),
                                             ctypes.POINTER(_p), ctypes.POINTER(_p), _i32, _i32, _i32, _i32, _i32,
@@ -371,6 +376,31 @@ def partial_attn_multi(q, q_pos, cu_q, ks, vs, k_poss, cu_ks, max_q: int, scale:
         arr(cu_ks, "cu_k"), num_seqs, int(max_q), hq, hkv, d, _dtype_code(q), float(scale),
         MASK_CAUSAL if causal else MASK_NONE, arr(outs, "out"), _dtype_code(outs[0]), arr(lses, "lse"),
         _dev(workspace, "workspace"), 0 if workspace is None else workspace.numel() * workspace.element_size(),
+        _stream(stream)))
+    return outs, lses
+
+
+def partial_attn_multi_noalloc(q, q_pos, cu_q, ks, vs, k_poss, cu_ks, max_q: int, scale: float, outs, lses,
+                               causal: bool = True, stream=None):
+    """partial_attn_multi without any allocation: the launch order lives in the
+    library's own device scratch (at most 8192 tile units). The caller passes
+    every output (outs[i], lses[i]). Returns (outs, lses)."""
+    tq, hq, d = _check_q(q)
+    n = len(ks)
+    if outs is None or lses is None or len(outs) != n or len(lses) != n:
+        raise ValueError("the no-allocation call needs one caller-allocated output and LSE per shard")
+    hkv, num_seqs = _check_shards(q, q_pos, cu_q, ks, vs, k_poss, cu_ks, causal)
+    for i in range(n):
+        _check_outputs(q, outs[i], lses[i], f"outs[{i}]", f"lses[{i}]")
+        if outs[i].dtype != outs[0].dtype:
+            raise ValueError("every partial output needs the same dtype")
+    _same_device(("q", q), *[(f"outs[{i}]", t) for i, t in enumerate(outs)],
+                 *[(f"lses[{i}]", t) for i, t in enumerate(lses)])
+    arr = lambda ts, name: (_p * n)(*[_dev(t, name) for t in ts])  # noqa: E731
+    _check("cpa_partial_attn_multi_noalloc", load_library().cpa_partial_attn_multi_noalloc(
+        n, _dev(q, "q"), _dev(q_pos, "q_pos"), _dev(cu_q, "cu_q"), arr(ks, "k"), arr(vs, "v"), arr(k_poss, "k_pos"),
+        arr(cu_ks, "cu_k"), num_seqs, int(max_q), hq, hkv, d, _dtype_code(q), float(scale),
+        MASK_CAUSAL if causal else MASK_NONE, arr(outs, "out"), _dtype_code(outs[0]), arr(lses, "lse"),
         _stream(stream)))
     return outs, lses
 

@@ -78,14 +78,14 @@ extern "C" cpa_status cpa_partial_attn_multi_workspace(int32_t n_shards, int32_t
   return CPA_OK;
 }
 
-extern "C" cpa_status cpa_partial_attn_multi(int32_t n_shards, const void* q, const int32_t* q_pos,
-                                             const int32_t* cu_q, const void* const* k, const void* const* v,
-                                             const int32_t* const* k_pos, const int32_t* const* cu_k,
-                                             int32_t num_seqs, int32_t max_q, int32_t hq, int32_t hkv, int32_t d,
-                                             cpa_dtype in_dtype, float scale, cpa_mask mask, void* const* o,
-                                             cpa_dtype o_dtype, float* const* lse, void* workspace,
-                                             size_t workspace_bytes, void* stream) {
-  const char* fn = "cpa_partial_attn_multi";
+namespace {
+
+// Validation and argument setup shared by the batched pass-KV calls.
+cpa_status prepare_multi(const char* fn, int32_t n_shards, const void* q, const int32_t* q_pos, const int32_t* cu_q,
+                         const void* const* k, const void* const* v, const int32_t* const* k_pos,
+                         const int32_t* const* cu_k, int32_t num_seqs, int32_t max_q, int32_t hq, int32_t hkv,
+                         int32_t d, cpa_dtype in_dtype, float scale, cpa_mask mask, void* const* o,
+                         cpa_dtype o_dtype, float* const* lse, AttnArgs* args) {
   if (n_shards < 1 || n_shards > kMaxShards)
     return fail(CPA_ERR_INVALID_ARG, "%s: n_shards %d not in [1, %d]", fn, n_shards, kMaxShards);
   if (!k || !v || !cu_k || !o || !lse || (mask == CPA_MASK_CAUSAL && !k_pos))
@@ -94,7 +94,6 @@ extern "C" cpa_status cpa_partial_attn_multi(int32_t n_shards, const void* q, co
   if (o_dtype != CPA_BF16 && o_dtype != CPA_F32) return fail(CPA_ERR_INVALID_ARG, "%s: bad o_dtype", fn);
   if (in_dtype == CPA_F32 && o_dtype != CPA_F32)
     return fail(CPA_ERR_UNSUPPORTED, "%s: fp32 inputs need an fp32 output", fn);
-  AttnArgs args[kMaxShards];
   for (int i = 0; i < n_shards; ++i) {
     const int32_t* kp = (mask == CPA_MASK_CAUSAL) ? k_pos[i] : nullptr;
     cpa_status st = check_common(fn, q, q_pos, cu_q, k[i], v[i], num_seqs, max_q, hq, hkv, d, scale, mask, o[i], lse[i]);
@@ -122,17 +121,66 @@ extern "C" cpa_status cpa_partial_attn_multi(int32_t n_shards, const void* q, co
     a.o_bf16 = o_dtype == CPA_BF16;
     a.lse = lse[i];
   }
-  cpa_status st = check_device();
-  if (st != CPA_OK) return st;
-  if (num_seqs == 0 || max_q == 0) return CPA_OK;
-  hipStream_t s = (hipStream_t)stream;
+  return CPA_OK;
+}
+
+// The batched launch: one launch over every shard (bf16, even GQA group), or
+// one launch per shard otherwise.
+cpa_status run_multi(const AttnArgs* args, int32_t n_shards, cpa_dtype in_dtype, void* order_ws,
+                     size_t order_ws_bytes, hipStream_t s) {
   if (in_dtype == CPA_BF16 && attn_pp_supported(args[0]))
-    return launch_attn_pp(args, n_shards, /*paged=*/false, s, workspace, workspace_bytes);
+    return launch_attn_pp(args, n_shards, /*paged=*/false, s, order_ws, order_ws_bytes);
   for (int i = 0; i < n_shards; ++i) {
-    st = (in_dtype == CPA_F32) ? launch_attn_f32(args[i], s) : launch_attn_mfma(args[i], /*paged=*/false, s);
+    const cpa_status st =
+        (in_dtype == CPA_F32) ? launch_attn_f32(args[i], s) : launch_attn_mfma(args[i], /*paged=*/false, s);
     if (st != CPA_OK) return st;
   }
   return CPA_OK;
+}
+
+}  // namespace
+
+extern "C" cpa_status cpa_partial_attn_multi(int32_t n_shards, const void* q, const int32_t* q_pos,
+                                             const int32_t* cu_q, const void* const* k, const void* const* v,
+                                             const int32_t* const* k_pos, const int32_t* const* cu_k,
+                                             int32_t num_seqs, int32_t max_q, int32_t hq, int32_t hkv, int32_t d,
+                                             cpa_dtype in_dtype, float scale, cpa_mask mask, void* const* o,
+                                             cpa_dtype o_dtype, float* const* lse, void* workspace,
+                                             size_t workspace_bytes, void* stream) {
+  AttnArgs args[kMaxShards];
+  cpa_status st = prepare_multi("cpa_partial_attn_multi", n_shards, q, q_pos, cu_q, k, v, k_pos, cu_k, num_seqs,
+                                max_q, hq, hkv, d, in_dtype, scale, mask, o, o_dtype, lse, args);
+  if (st != CPA_OK) return st;
+  st = check_device();
+  if (st != CPA_OK) return st;
+  if (num_seqs == 0 || max_q == 0) return CPA_OK;
+  return run_multi(args, n_shards, in_dtype, workspace, workspace_bytes, (hipStream_t)stream);
+}
+
+extern "C" cpa_status cpa_partial_attn_multi_noalloc(int32_t n_shards, const void* q, const int32_t* q_pos,
+                                                     const int32_t* cu_q, const void* const* k, const void* const* v,
+                                                     const int32_t* const* k_pos, const int32_t* const* cu_k,
+                                                     int32_t num_seqs, int32_t max_q, int32_t hq, int32_t hkv,
+                                                     int32_t d, cpa_dtype in_dtype, float scale, cpa_mask mask,
+                                                     void* const* o, cpa_dtype o_dtype, float* const* lse,
+                                                     void* stream) {
+  const char* fn = "cpa_partial_attn_multi_noalloc";
+  AttnArgs args[kMaxShards];
+  cpa_status st = prepare_multi(fn, n_shards, q, q_pos, cu_q, k, v, k_pos, cu_k, num_seqs, max_q, hq, hkv, d,
+                                in_dtype, scale, mask, o, o_dtype, lse, args);
+  if (st != CPA_OK) return st;
+  const int64_t units = attn_pp_tile_units(n_shards, num_seqs, max_q);
+  if (units > attn_pp_scratch_units())
+    return fail(CPA_ERR_CAPACITY, "%s: %lld tile units (query tiles x sequences x shards); at most %d fit the "
+                "library's launch-order scratch", fn, (long long)units, attn_pp_scratch_units());
+  st = check_device();
+  if (st != CPA_OK) return st;
+  if (num_seqs == 0 || max_q == 0) return CPA_OK;
+  void* scratch_ptr = nullptr;
+  size_t scratch_bytes = 0;
+  st = attn_pp_scratch(&scratch_ptr, &scratch_bytes);
+  if (st != CPA_OK) return st;
+  return run_multi(args, n_shards, in_dtype, scratch_ptr, scratch_bytes, (hipStream_t)stream);
 }
 
 extern "C" cpa_status cpa_partial_attn_merged(int32_t n_shards, const void* q, const int32_t* q_pos,

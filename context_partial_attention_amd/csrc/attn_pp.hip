@@ -41,6 +41,7 @@
 // of writing it. An optional pre-pass (pp_schedule_kernel) orders the launch
 // heaviest query tile first. Paged shards (pass-Q prefill) take one shard.
 #include <climits>
+#include <mutex>
 
 #include "attn_pp_common.h"
 
@@ -659,6 +660,12 @@ __global__ __launch_bounds__(kSchedThreads) void pp_schedule_kernel(PPParams p, 
   }
 }
 
+// Launch-order scratch of cpa_partial_attn_multi_noalloc: one entry per tile
+// unit, written in full by the pre-pass before the attention kernel reads it.
+// Host code never uses this name as an address: the address comes from
+// hipGetSymbolAddress (attn_pp_scratch), per device.
+static __device__ __align__(256) int scratch[kSchedMaxUnits];
+
 template <int D, bool PAGED, bool OUT_BF16, bool MERGED = false>
 void pp_launch(const PPParams& p, uint32_t blocks, hipStream_t st) {
   hipLaunchKernelGGL((attn_pp_kernel<D, PAGED, OUT_BF16, MERGED>), dim3(blocks), dim3(kThreads), 0, st, p);
@@ -668,8 +675,34 @@ void pp_launch(const PPParams& p, uint32_t blocks, hipStream_t st) {
 
 bool attn_pp_supported(const AttnArgs& a) { return (a.hq / a.hkv) % 2 == 0; }
 
+int attn_pp_scratch_units() { return kSchedMaxUnits; }
+
+cpa_status attn_pp_scratch(void** ptr, size_t* bytes) {
+  static std::mutex mu;
+  static void* addr[64] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(CPA_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= 64) return fail(CPA_ERR_UNSUPPORTED, "device index %d out of range", dev);
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    void* a = nullptr;
+    e = hipGetSymbolAddress(&a, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !a)
+      return fail(CPA_ERR_HIP, "hipGetSymbolAddress(scratch) on device %d: %s", dev, hipGetErrorString(e));
+    addr[dev] = a;
+  }
+  *ptr = addr[dev];
+  *bytes = sizeof(scratch);
+  return CPA_OK;
+}
+
+int64_t attn_pp_tile_units(int n_shards, int num_seqs, int max_q) {
+  return cdiv(max_q, kRows) * (int64_t)num_seqs * n_shards;
+}
+
 size_t attn_pp_order_bytes(int n_shards, int num_seqs, int max_q) {
-  const int64_t units = cdiv(max_q, kRows) * (int64_t)num_seqs * n_shards;
+  const int64_t units = attn_pp_tile_units(n_shards, num_seqs, max_q);
   if (units <= 0 || units > kSchedMaxUnits) return 0;
   return (size_t)cdiv(units * (int64_t)sizeof(int), 256) * 256;
 }

@@ -77,6 +77,13 @@ struct MergedOut {
 };
 bool attn_pp_supported(const AttnArgs& a);
 size_t attn_pp_order_bytes(int n_shards, int num_seqs, int max_q);
+// Tile units (query tiles x sequences x shards) the launch-order pre-pass sorts.
+int64_t attn_pp_tile_units(int n_shards, int num_seqs, int max_q);
+// The library's own launch-order scratch (a device array in attn_pp.hip, one
+// copy per GPU): its address on the current device, looked up once per device,
+// and the number of tile units it holds.
+cpa_status attn_pp_scratch(void** ptr, size_t* bytes);
+int attn_pp_scratch_units();
 // With `accum` (one contiguous shard), the partial is folded into the running
 // (o_acc, lse_acc) in place; o_out (may be NULL) gets a copy of the merged O in
 // the shard's output dtype.

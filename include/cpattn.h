@@ -247,6 +247,32 @@ cpa_status cpa_partial_attn_multi(int32_t n_shards, const void* q, const int32_t
                                   void* workspace, size_t workspace_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------
+ * cpa_partial_attn_multi_noalloc — cpa_partial_attn_multi for callers that
+ * cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid allocation): the same results, with the
+ * launch-order workspace taken from a scratch array the library holds in each
+ * GPU's memory (8192 tile units, 32 KiB) instead of a caller buffer. Calls no
+ * allocating routine.
+ *
+ * In / out: as cpa_partial_attn_multi without workspace arguments.
+ * Limit: cdiv(max_q, 128) * num_seqs * n_shards <= 8192 tile units;
+ *   larger problems get CPA_ERR_CAPACITY (use cpa_partial_attn_multi).
+ * Every call on one GPU shares that GPU's scratch array (the pre-pass rewrites
+ * all of it that a call uses): calls that overlap on one GPU, on different
+ * streams say, race and must be serialised by the caller.
+ * Errors: as cpa_partial_attn_multi; CPA_ERR_CAPACITY as above; CPA_ERR_HIP if
+ *   the scratch address cannot be obtained on the current device.
+ * ------------------------------------------------------------------------- */
+cpa_status cpa_partial_attn_multi_noalloc(int32_t n_shards, const void* q, const int32_t* q_pos,
+                                          const int32_t* cu_q, const void* const* k,
+                                          const void* const* v, const int32_t* const* k_pos,
+                                          const int32_t* const* cu_k, int32_t num_seqs,
+                                          int32_t max_q, int32_t hq, int32_t hkv, int32_t d,
+                                          cpa_dtype in_dtype, float scale, cpa_mask mask,
+                                          void* const* o, cpa_dtype o_dtype, float* const* lse,
+                                          void* stream);
+
+/* ---------------------------------------------------------------------------
  * cpa_partial_attn_merged — the merged result of the pass-KV steps over
  * n_shards resident contiguous KV shards, computed in one walk (device).
  *
