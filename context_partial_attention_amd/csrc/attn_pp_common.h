@@ -1,4 +1,4 @@
-// Shared pieces of the bf16 prefill kernels (attn_pp.hip, attn_pair.hip):
+// Shared pieces of the bf16 prefill kernel (attn_pp.hip) and its helpers:
 // tile geometry and LDS layout of the K/V tiles, the kernel parameters, the
 // launch-order encoding, and small device helpers. Internal to the library.
 #pragma once
@@ -146,10 +146,6 @@ __device__ int pp_count_le(const int* __restrict__ a, int n, int x) {
   }
 }
 
-// Launches of the one-wave-per-SIMD kernel (attn_pair.hip): the same units,
-// grid and parameters as attn_pp_kernel, one workgroup of 4 waves per unit.
-constexpr int kPairThreads = 256;
-void pair_launch(const PPParams& p, uint32_t blocks, int d, bool paged, bool o_bf16, bool merged, hipStream_t st);
 
 }  // namespace pp
 }  // namespace cpa
