@@ -101,11 +101,22 @@ def bench_workload(name: str, steps: int, warmup: int, next_rows: bool = True) -
         for r in range(w.cp):
             if r != w.rank:
                 run.partial(r)
-        launches = [lambda: run.partial(w.rank)]
+        if w.kind == "decode":
+            # decode: the received partials are merged inside the rank's own
+            # decode launches (split kernel + merge kernel), no merge launch;
+            # the rank's own partial is written once, for the separate merge
+            # timed below for comparison
+            run.partial(w.rank)
+            launches = [lambda: run.decode_fold(own=False)]
+        else:
+            launches = [lambda: run.partial(w.rank)]
+    merge_in_step = w.kind != "decode"
+
     def step():
         for f in launches:
             f()
-        run.merge()
+        if merge_in_step:
+            run.merge()
 
     for _ in range(warmup):
         step()
@@ -222,22 +233,28 @@ def bench_workload(name: str, steps: int, warmup: int, next_rows: bool = True) -
         res["partial_TFLOPs"] = sum(flops) / (sum(part_ms) * 1e-3) / 1e12
         res["partial_pct_bf16_peak"] = 100 * res["partial_TFLOPs"] / PEAK_BF16_TFLOPS
     else:
-        # decode: K and V of every visible local token, q, O (fp32) and LSE
-        rk = inp["ranks"][w.rank]
+        # decode step (the rank's split and merge launches): K and V of every
+        # visible local token, q, the cp-1 received partials (fp32 O + LSE)
+        # and the merged O and LSE
         kv_bytes = 2 * w.hkv * w.d * 2 * pairs[0]  # one query per sequence: pairs == visible tokens
         nq = inp["q"].shape[0]
-        io_bytes = nq * w.hq * w.d * 2 + nq * w.hq * (w.d * 4 + 4)
-        part_bytes = kv_bytes + io_bytes
-        res["partial_bytes"] = int(part_bytes)
-        res["partial_GBps"] = part_bytes / (res["partial_ms"][0] * 1e-3) / 1e9
+        out_bytes = 2 if run.merged_dtype == torch.bfloat16 else 4
+        io_bytes = (nq * w.hq * w.d * 2 + (w.cp - 1) * nq * w.hq * (w.d * 4 + 4)
+                    + nq * w.hq * (w.d * out_bytes + 4))
+        step_bytes = kv_bytes + io_bytes
+        res["step_bytes"] = int(step_bytes)
+        res["partial_GBps"] = step_bytes / (res["partial_ms"][0] * 1e-3) / 1e9
         res["partial_hbm_frac"] = res["partial_GBps"] / PEAK_HBM_GBS
         cold = cold_launch_ms(launches[0])
         res["partial_cold_ms"] = cold
-        res["partial_cold_GBps"] = part_bytes / (cold * 1e-3) / 1e9
+        res["partial_cold_GBps"] = step_bytes / (cold * 1e-3) / 1e9
         res["partial_cold_hbm_frac"] = res["partial_cold_GBps"] / PEAK_HBM_GBS
-        res["GBps"] = (part_bytes + mbytes) / (res["ms_per_step"] * 1e-3) / 1e9
+        res["GBps"] = step_bytes / (res["ms_per_step"] * 1e-3) / 1e9
         res["hbm_frac"] = res["GBps"] / PEAK_HBM_GBS
-        del rk
+        # the separate cp-way merge launch the fold replaces, timed on its own
+        # for comparison (not part of the step)
+        for k in [k for k in res if k.startswith("merge_")]:
+            res["unfolded_" + k] = res.pop(k)
     if w.kind == "pass_kv":
         res["seq_lens"] = inp["lens"]
         if next_rows and w.dtype == torch.bfloat16 and (w.hq // w.hkv) % 2 == 0:

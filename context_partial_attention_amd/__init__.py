@@ -25,6 +25,7 @@ from .binding import (  # noqa: F401
     partial_attn_multi_noalloc,
     partial_attn_multi_workspace,
     partial_attn_paged,
+    partial_attn_paged_merged,
     partial_attn_paged_workspace,
     pass_cost,
     rr_placement,

@@ -98,6 +98,11 @@ def load_library():
     lib.cpa_partial_attn_paged.argtypes = [_p, _p, _p, _p, _p, _p, _i32, _p, _i32, _i32, _i32, _i32, _i32, _i32,
                                            _i32, _i32, _i32, _i32, _f32, _i32, _p, _i32, _p, _p, ctypes.c_size_t,
                                            _p]
+    lib.cpa_partial_attn_paged_merged.restype = _i32
+    lib.cpa_partial_attn_paged_merged.argtypes = [_p, _p, _p, _p, _p, _p, _i32, _p, _i32, _i32, _i32, _i32, _i32,
+                                                  _i32, _i32, _i32, _i32, _i32, _f32, _i32, _i32, ctypes.POINTER(_p),
+                                                  ctypes.POINTER(_p), _i32, _p, _p, _p, _i32, _p, _p,
+                                                  ctypes.c_size_t, _p]
     lib.cpa_lse_merge.restype = _i32
     lib.cpa_lse_merge.argtypes = [_i32, ctypes.POINTER(_p), ctypes.POINTER(_p), _i32, _i64, _i32, _p, _i32, _p, _p]
     _lib = lib
@@ -464,10 +469,8 @@ def partial_attn_paged_workspace(num_seqs: int, max_q: int, max_blocks: int, blo
     return n.value
 
 
-def partial_attn_paged(q, q_pos, cu_q, k_cache, v_cache, block_table, local_kv_lens, cp_size: int, cp_rank: int,
-                       interleave: int, max_q: int, scale: float, causal: bool = True, out=None, lse=None,
-                       out_dtype=None, workspace=None, stream=None):
-    """Q against one rank's paged round-robin KV shard (k/v cache [blocks,hkv,16,d]). Returns (o, lse)."""
+def _check_paged(q, q_pos, cu_q, k_cache, v_cache, block_table, local_kv_lens, causal):
+    """Validates the paged-shard arguments; returns (num_seqs, hkv, block_size, max_blocks)."""
     torch = _torch()
     tq, hq, d = _check_q(q)
     if k_cache.dim() != 4 or k_cache.shape[3] != d:
@@ -482,7 +485,17 @@ def partial_attn_paged(q, q_pos, cu_q, k_cache, v_cache, block_table, local_kv_l
         raise ValueError(f"block_table must be [num_seqs={num_seqs}, max_blocks] int32")
     _shape(block_table, "block_table", block_table.shape, torch.int32)
     _shape(local_kv_lens, "local_kv_lens", (num_seqs,), torch.int32)
-    max_blocks = block_table.shape[1]
+    return num_seqs, hkv, block_size, block_table.shape[1]
+
+
+def partial_attn_paged(q, q_pos, cu_q, k_cache, v_cache, block_table, local_kv_lens, cp_size: int, cp_rank: int,
+                       interleave: int, max_q: int, scale: float, causal: bool = True, out=None, lse=None,
+                       out_dtype=None, workspace=None, stream=None):
+    """Q against one rank's paged round-robin KV shard (k/v cache [blocks,hkv,16,d]). Returns (o, lse)."""
+    torch = _torch()
+    tq, hq, d = _check_q(q)
+    num_seqs, hkv, block_size, max_blocks = _check_paged(q, q_pos, cu_q, k_cache, v_cache, block_table,
+                                                         local_kv_lens, causal)
     out_dtype = out_dtype or torch.float32
     if out is None:
         out = torch.empty((tq, hq, d), dtype=out_dtype, device=q.device)
@@ -504,6 +517,64 @@ def partial_attn_paged(q, q_pos, cu_q, k_cache, v_cache, block_table, local_kv_l
         cp_rank, interleave, num_seqs, int(max_q), hq, hkv, d, _dtype_code(q), float(scale),
         MASK_CAUSAL if causal else MASK_NONE, _dev(out, "out"), _dtype_code(out), _dev(lse, "lse"),
         _dev(workspace, "workspace"), ws_bytes, _stream(stream)))
+    return out, lse
+
+
+def partial_attn_paged_merged(q, q_pos, cu_q, k_cache, v_cache, block_table, local_kv_lens, cp_size: int,
+                              cp_rank: int, interleave: int, max_q: int, scale: float, o_parts, lse_parts,
+                              causal: bool = True, out=None, lse=None, out_dtype=None, own_out=None, own_lse=None,
+                              workspace=None, stream=None):
+    """Decode (max_q <= 1): this rank's partial against its paged shard, merged
+    in the same call with the other ranks' partials o_parts[j] [Tq,hq,d],
+    lse_parts[j] [Tq,hq]. own_out / own_lse (optional) receive this rank's own
+    partial in the parts' dtype. Returns (o, lse)."""
+    torch = _torch()
+    tq, hq, d = _check_q(q)
+    num_seqs, hkv, block_size, max_blocks = _check_paged(q, q_pos, cu_q, k_cache, v_cache, block_table,
+                                                         local_kv_lens, causal)
+    if int(max_q) > 1:
+        raise ValueError(f"partial_attn_paged_merged is for decode (max_q <= 1), got max_q = {max_q}")
+    n = len(o_parts)
+    if n != len(lse_parts) or n > 15:
+        raise ValueError("need the same number (at most 15) of O and LSE parts")
+    part_dtype = o_parts[0].dtype if n else (own_out.dtype if own_out is not None else torch.float32)
+    if part_dtype not in (torch.float32, torch.bfloat16):
+        raise ValueError(f"O parts have dtype {part_dtype}, expected float32 or bfloat16")
+    for j in range(n):
+        _shape(o_parts[j], f"o_parts[{j}]", (tq, hq, d), part_dtype)
+        _shape(lse_parts[j], f"lse_parts[{j}]", (tq, hq), torch.float32)
+    if own_out is not None:
+        _shape(own_out, "own_out", (tq, hq, d), part_dtype)
+    if own_lse is not None:
+        _shape(own_lse, "own_lse", (tq, hq), torch.float32)
+    out_dtype = out_dtype or torch.float32
+    if out is None:
+        out = torch.empty((tq, hq, d), dtype=out_dtype, device=q.device)
+    if lse is None:
+        lse = torch.empty((tq, hq), dtype=torch.float32, device=q.device)
+    _check_outputs(q, out, lse)
+    _check_workspace(workspace)
+    _same_device(("q", q), ("q_pos", q_pos), ("cu_q", cu_q), ("k_cache", k_cache), ("v_cache", v_cache),
+                 ("block_table", block_table), ("local_kv_lens", local_kv_lens), ("out", out), ("lse", lse),
+                 ("workspace", workspace), ("own_out", own_out), ("own_lse", own_lse),
+                 *[(f"o_parts[{j}]", t) for j, t in enumerate(o_parts)],
+                 *[(f"lse_parts[{j}]", t) for j, t in enumerate(lse_parts)])
+    need = partial_attn_paged_workspace(num_seqs, int(max_q), max_blocks, block_size, hq, d)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    optrs = (_p * max(n, 1))(*[_dev(o, "o_part") for o in o_parts])
+    lptrs = (_p * max(n, 1))(*[_dev(t, "lse_part") for t in lse_parts])
+    lib = load_library()
+    _check("cpa_partial_attn_paged_merged", lib.cpa_partial_attn_paged_merged(
+        _dev(q, "q"), _dev(q_pos, "q_pos"), _dev(cu_q, "cu_q"), _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"),
+        _dev(block_table, "block_table"), max_blocks, _dev(local_kv_lens, "local_kv_lens"), block_size, cp_size,
+        cp_rank, interleave, num_seqs, int(max_q), hq, hkv, d, _dtype_code(q), float(scale),
+        MASK_CAUSAL if causal else MASK_NONE, n, optrs, lptrs,
+        BF16 if part_dtype == torch.bfloat16 else F32,
+        None if own_out is None else _dev(own_out, "own_out"), None if own_lse is None else _dev(own_lse, "own_lse"),
+        _dev(out, "out"), _dtype_code(out), _dev(lse, "lse"), _dev(workspace, "workspace"), ws_bytes,
+        _stream(stream)))
     return out, lse
 
 

@@ -288,14 +288,16 @@ extern "C" cpa_status cpa_partial_attn_paged_workspace(int32_t num_seqs, int32_t
   return CPA_OK;
 }
 
-extern "C" cpa_status cpa_partial_attn_paged(const void* q, const int32_t* q_pos, const int32_t* cu_q,
-                                             const void* k_cache, const void* v_cache, const int32_t* block_table,
-                                             int32_t max_blocks, const int32_t* local_kv_lens, int32_t block_size,
-                                             int32_t cp_size, int32_t cp_rank, int32_t interleave, int32_t num_seqs,
-                                             int32_t max_q, int32_t hq, int32_t hkv, int32_t d, cpa_dtype in_dtype,
-                                             float scale, cpa_mask mask, void* o, cpa_dtype o_dtype, float* lse,
-                                             void* workspace, size_t workspace_bytes, void* stream) {
-  const char* fn = "cpa_partial_attn_paged";
+// Checks of the paged entry points and their arguments; num_seqs == 0 or
+// max_q == 0 leaves *empty true (nothing to launch).
+static cpa_status prepare_paged(const char* fn, const void* q, const int32_t* q_pos, const int32_t* cu_q,
+                                const void* k_cache, const void* v_cache, const int32_t* block_table,
+                                int32_t max_blocks, const int32_t* local_kv_lens, int32_t block_size,
+                                int32_t cp_size, int32_t cp_rank, int32_t interleave, int32_t num_seqs,
+                                int32_t max_q, int32_t hq, int32_t hkv, int32_t d, cpa_dtype in_dtype, float scale,
+                                cpa_mask mask, void* o, cpa_dtype o_dtype, float* lse, void* workspace,
+                                size_t workspace_bytes, AttnArgs* a, bool* empty) {
+  *empty = true;
   cpa_status st =
       check_common(fn, q, q_pos, cu_q, k_cache, v_cache, num_seqs, max_q, hq, hkv, d, scale, mask, o, lse);
   if (st != CPA_OK) return st;
@@ -312,8 +314,7 @@ extern "C" cpa_status cpa_partial_attn_paged(const void* q, const int32_t* q_pos
     return fail(CPA_ERR_INVALID_ARG, "%s: block_table or local_kv_lens is NULL", fn);
   if (num_seqs > 0 && max_q > 0 && !local_kv_lens)
     return fail(CPA_ERR_INVALID_ARG, "%s: local_kv_lens is NULL", fn);
-  const bool decode = max_q == 1;
-  if (decode) {
+  if (max_q == 1) {
     const size_t need = decode_workspace_bytes(num_seqs, max_blocks, block_size, hq, d);
     if (workspace_bytes < need)
       return fail(CPA_ERR_CAPACITY, "%s: workspace has %zu bytes, decode needs %zu", fn, workspace_bytes, need);
@@ -322,31 +323,79 @@ extern "C" cpa_status cpa_partial_attn_paged(const void* q, const int32_t* q_pos
   st = check_device();
   if (st != CPA_OK) return st;
   if (num_seqs == 0 || max_q == 0) return CPA_OK;
+  *empty = false;
+  a->q = q;
+  a->q_pos = q_pos;
+  a->cu_q = cu_q;
+  a->k = k_cache;
+  a->v = v_cache;
+  a->block_table = block_table;
+  a->max_blocks = max_blocks;
+  a->local_kv_lens = local_kv_lens;
+  a->cp = cp_size;
+  a->rank = cp_rank;
+  a->interleave = interleave;
+  a->num_seqs = num_seqs;
+  a->max_q = max_q;
+  a->hq = hq;
+  a->hkv = hkv;
+  a->d = d;
+  a->scale = scale;
+  a->causal = mask == CPA_MASK_CAUSAL;
+  a->o = o;
+  a->o_bf16 = o_dtype == CPA_BF16;
+  a->lse = lse;
+  a->workspace = workspace;
+  a->workspace_bytes = workspace_bytes;
+  return CPA_OK;
+}
+
+extern "C" cpa_status cpa_partial_attn_paged(const void* q, const int32_t* q_pos, const int32_t* cu_q,
+                                             const void* k_cache, const void* v_cache, const int32_t* block_table,
+                                             int32_t max_blocks, const int32_t* local_kv_lens, int32_t block_size,
+                                             int32_t cp_size, int32_t cp_rank, int32_t interleave, int32_t num_seqs,
+                                             int32_t max_q, int32_t hq, int32_t hkv, int32_t d, cpa_dtype in_dtype,
+                                             float scale, cpa_mask mask, void* o, cpa_dtype o_dtype, float* lse,
+                                             void* workspace, size_t workspace_bytes, void* stream) {
   AttnArgs a;
-  a.q = q;
-  a.q_pos = q_pos;
-  a.cu_q = cu_q;
-  a.k = k_cache;
-  a.v = v_cache;
-  a.block_table = block_table;
-  a.max_blocks = max_blocks;
-  a.local_kv_lens = local_kv_lens;
-  a.cp = cp_size;
-  a.rank = cp_rank;
-  a.interleave = interleave;
-  a.num_seqs = num_seqs;
-  a.max_q = max_q;
-  a.hq = hq;
-  a.hkv = hkv;
-  a.d = d;
-  a.scale = scale;
-  a.causal = mask == CPA_MASK_CAUSAL;
-  a.o = o;
-  a.o_bf16 = o_dtype == CPA_BF16;
-  a.lse = lse;
-  a.workspace = workspace;
-  a.workspace_bytes = workspace_bytes;
+  bool empty;
+  cpa_status st = prepare_paged("cpa_partial_attn_paged", q, q_pos, cu_q, k_cache, v_cache, block_table, max_blocks,
+                                local_kv_lens, block_size, cp_size, cp_rank, interleave, num_seqs, max_q, hq, hkv,
+                                d, in_dtype, scale, mask, o, o_dtype, lse, workspace, workspace_bytes, &a, &empty);
+  if (st != CPA_OK || empty) return st;
   hipStream_t s = (hipStream_t)stream;
-  if (decode) return launch_attn_decode(a, s);
+  if (max_q == 1) return launch_attn_decode(a, s);
   return attn_pp_supported(a) ? launch_attn_pp(&a, 1, /*paged=*/true, s) : launch_attn_mfma(a, /*paged=*/true, s);
+}
+
+extern "C" cpa_status cpa_partial_attn_paged_merged(
+    const void* q, const int32_t* q_pos, const int32_t* cu_q, const void* k_cache, const void* v_cache,
+    const int32_t* block_table, int32_t max_blocks, const int32_t* local_kv_lens, int32_t block_size,
+    int32_t cp_size, int32_t cp_rank, int32_t interleave, int32_t num_seqs, int32_t max_q, int32_t hq, int32_t hkv,
+    int32_t d, cpa_dtype in_dtype, float scale, cpa_mask mask, int32_t n_parts, const void* const* o_parts,
+    const float* const* lse_parts, cpa_dtype part_dtype, void* own_o, float* own_lse, void* o, cpa_dtype o_dtype,
+    float* lse, void* workspace, size_t workspace_bytes, void* stream) {
+  const char* fn = "cpa_partial_attn_paged_merged";
+  if (max_q > 1) return fail(CPA_ERR_UNSUPPORTED, "%s: decode only (max_q <= 1), got max_q = %d", fn, max_q);
+  if (n_parts < 0 || n_parts > kMaxFoldParts)
+    return fail(CPA_ERR_INVALID_ARG, "%s: n_parts %d not in [0, %d]", fn, n_parts, kMaxFoldParts);
+  if (n_parts > 0 && (!o_parts || !lse_parts)) return fail(CPA_ERR_INVALID_ARG, "%s: part arrays are NULL", fn);
+  if (part_dtype != CPA_BF16 && part_dtype != CPA_F32) return fail(CPA_ERR_INVALID_ARG, "%s: bad part_dtype", fn);
+  AttnArgs a;
+  bool empty;
+  cpa_status st = prepare_paged(fn, q, q_pos, cu_q, k_cache, v_cache, block_table, max_blocks, local_kv_lens,
+                                block_size, cp_size, cp_rank, interleave, num_seqs, max_q, hq, hkv, d, in_dtype,
+                                scale, mask, o, o_dtype, lse, workspace, workspace_bytes, &a, &empty);
+  if (st != CPA_OK || empty) return st;
+  DecodeFold f{};
+  f.n = n_parts;
+  for (int j = 0; j < n_parts; ++j) {
+    if (!o_parts[j] || !lse_parts[j]) return fail(CPA_ERR_INVALID_ARG, "%s: part %d pointer is NULL", fn, j);
+    f.o[j] = o_parts[j];
+    f.lse[j] = lse_parts[j];
+  }
+  f.part_bf16 = part_dtype == CPA_BF16;
+  f.own_o = own_o;
+  f.own_lse = own_lse;
+  return launch_attn_decode(a, (hipStream_t)stream, &f);
 }

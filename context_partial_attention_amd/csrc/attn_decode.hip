@@ -9,7 +9,10 @@
 // shard is read once. The work is split over (sequence, KV head, split of
 // 512 local tokens) so that sequences of very different lengths still fill
 // the GPU, and a second small kernel merges the splits of each (sequence,
-// head) with the same exact LSE rule used across ranks.
+// head) with the same exact LSE rule used across ranks. That kernel can also
+// fold in the other ranks' partials of the same rows when they are already
+// resident (received), so that a rank's decode step ends with the merged
+// result after two launches, without a separate cross-rank merge.
 //
 // Inside a workgroup (4 waves, each walking every 4th 16-token block):
 //  * S^T = K q^T with v_mfma_f32_16x16x32_bf16: the 16 keys of a block are the
@@ -48,6 +51,12 @@ struct DecParams {
   float* ws_lse;  // [num_seqs][hq][n_splits_max], base-2 LSE of each split
   void* o;
   float* lse;
+  // other ranks' partials of the same rows, folded in by the merge kernel
+  int n_fold;
+  const void* fold_o[kMaxFoldParts];
+  const float* fold_lse[kMaxFoldParts];
+  void* own_o;  // this rank's own partial (may be NULL), in the parts' dtype
+  float* own_lse;
 };
 
 // Local KV slots of `seq` visible to its query at packed row `row`: the round-
@@ -230,7 +239,22 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecParams p) {
   }
 }
 
-template <int D, bool OUT_BF16>
+template <int D, bool BF16>
+__device__ __forceinline__ void store_row_part(void* base, int64_t off, int lane, const float (&x)[D / 64]) {
+#pragma unroll
+  for (int i = 0; i < D / 64; ++i) {
+    if constexpr (BF16) ((__bf16*)base)[off + lane + 64 * i] = (__bf16)x[i];
+    else ((float*)base)[off + lane + 64 * i] = x[i];
+  }
+}
+
+// One wave per (sequence, query head): merges the splits of this rank's
+// partial. FOLD: then merges that partial with the other ranks' partials of
+// the same row (p.fold_o / fold_lse, PART_BF16 giving their dtype) by the same
+// exact LSE rule, writes the result to p.o / p.lse and this rank's own partial
+// to p.own_o / own_lse when those are set. A part whose LSE is -inf has no
+// visible key; its O is not read.
+template <int D, bool OUT_BF16, bool FOLD, bool PART_BF16>
 __global__ __launch_bounds__(kThreads) void decode_merge_kernel(DecParams p) {
   constexpr int kPer = D / 64;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -239,6 +263,14 @@ __global__ __launch_bounds__(kThreads) void decode_merge_kernel(DecParams p) {
   const int seq = (int)(item / p.hq), h = (int)(item % p.hq);
   const int row = p.cu_q[seq];
   if (p.cu_q[seq + 1] <= row) return;
+  const int64_t ri = (int64_t)row * p.hq + h;
+  // the other ranks' LSEs (base 2) are read first, so their latency overlaps
+  // the split loop
+  float lf[FOLD ? kMaxFoldParts : 1];
+  if constexpr (FOLD) {
+#pragma unroll
+    for (int j = 0; j < kMaxFoldParts; ++j) lf[j] = j < p.n_fold ? p.fold_lse[j][ri] * kLog2e : kNegInf;
+  }
   const int n_vis = visible_local(p, seq, row);
   const int n_splits = (n_vis + kSplit - 1) / kSplit;
   const int64_t slot0 = ((int64_t)seq * p.hq + h) * p.n_splits_max;
@@ -260,13 +292,41 @@ __global__ __launch_bounds__(kThreads) void decode_merge_kernel(DecParams p) {
       for (int i = 0; i < kPer; ++i) acc[i] = fmaf(w, src[lane + 64 * i], acc[i]);
     }
   }
-  const int64_t obase = ((int64_t)row * p.hq + h) * D;
+  if constexpr (FOLD) {
+    if (p.own_o) store_row_part<D, PART_BF16>(p.own_o, ri * D, lane, acc);
+    if (p.own_lse && lane == 0) p.own_lse[ri] = lse2 * kLn2;
+    float m = lse2;
 #pragma unroll
-  for (int i = 0; i < kPer; ++i) {
-    if constexpr (OUT_BF16) ((__bf16*)p.o)[obase + lane + 64 * i] = (__bf16)acc[i];
-    else ((float*)p.o)[obase + lane + 64 * i] = acc[i];
+    for (int j = 0; j < kMaxFoldParts; ++j) m = fmaxf(m, lf[j]);
+    if (m == kNegInf) {
+#pragma unroll
+      for (int i = 0; i < kPer; ++i) acc[i] = 0.f;
+      lse2 = kNegInf;
+    } else {
+      float sum = hw_exp2(lse2 - m);
+#pragma unroll
+      for (int j = 0; j < kMaxFoldParts; ++j) sum += hw_exp2(lf[j] - m);
+      const float lt = m + hw_log2(sum);
+      const float w_own = hw_exp2(lse2 - lt);
+#pragma unroll
+      for (int i = 0; i < kPer; ++i) acc[i] *= w_own;
+#pragma unroll
+      for (int j = 0; j < kMaxFoldParts; ++j) {
+        if (j >= p.n_fold || lf[j] == kNegInf) continue;  // wave-uniform
+        const float w = hw_exp2(lf[j] - lt);
+#pragma unroll
+        for (int i = 0; i < kPer; ++i) {
+          float x;
+          if constexpr (PART_BF16) x = (float)((const __bf16*)p.fold_o[j])[ri * D + lane + 64 * i];
+          else x = ((const float*)p.fold_o[j])[ri * D + lane + 64 * i];
+          acc[i] = fmaf(w, x, acc[i]);
+        }
+      }
+      lse2 = lt;
+    }
   }
-  if (lane == 0) p.lse[(int64_t)row * p.hq + h] = lse2 * kLn2;
+  store_row_part<D, OUT_BF16>(p.o, ri * D, lane, acc);
+  if (lane == 0) p.lse[ri] = lse2 * kLn2;
 }
 
 int head_chunk_for(int g) { return g >= 8 ? 8 : (g >= 4 ? 4 : (g >= 2 ? 2 : 1)); }
@@ -287,6 +347,21 @@ void launch_split_d(const DecParams& p, hipStream_t st) {
   }
 }
 
+template <int D>
+void launch_merge_d(const DecParams& p, bool o_bf16, const DecodeFold* fold, hipStream_t st) {
+  const dim3 grid((uint32_t)cdiv((int64_t)p.num_seqs * p.hq, kWaves)), block(kThreads);
+  if (!fold) {
+    if (o_bf16) hipLaunchKernelGGL((decode_merge_kernel<D, true, false, false>), grid, block, 0, st, p);
+    else hipLaunchKernelGGL((decode_merge_kernel<D, false, false, false>), grid, block, 0, st, p);
+  } else if (fold->part_bf16) {
+    if (o_bf16) hipLaunchKernelGGL((decode_merge_kernel<D, true, true, true>), grid, block, 0, st, p);
+    else hipLaunchKernelGGL((decode_merge_kernel<D, false, true, true>), grid, block, 0, st, p);
+  } else {
+    if (o_bf16) hipLaunchKernelGGL((decode_merge_kernel<D, true, true, false>), grid, block, 0, st, p);
+    else hipLaunchKernelGGL((decode_merge_kernel<D, false, true, false>), grid, block, 0, st, p);
+  }
+}
+
 }  // namespace
 
 size_t decode_workspace_bytes(int32_t num_seqs, int32_t max_blocks, int32_t block_size, int32_t hq, int32_t d) {
@@ -294,7 +369,7 @@ size_t decode_workspace_bytes(int32_t num_seqs, int32_t max_blocks, int32_t bloc
   return (size_t)num_seqs * hq * n_splits * (d + 1) * sizeof(float);
 }
 
-cpa_status launch_attn_decode(const AttnArgs& a, hipStream_t st) {
+cpa_status launch_attn_decode(const AttnArgs& a, hipStream_t st, const DecodeFold* fold) {
   DecParams p{};
   p.q = (const uint16_t*)a.q;
   p.q_pos = a.q_pos;
@@ -330,14 +405,17 @@ cpa_status launch_attn_decode(const AttnArgs& a, hipStream_t st) {
     cpa_status s = check_launch("cpa_partial_attn_paged (decode splits)");
     if (s != CPA_OK) return s;
   }
-  const uint32_t mblocks = (uint32_t)cdiv((int64_t)a.num_seqs * a.hq, kWaves);
-  if (a.d == 64) {
-    if (a.o_bf16) hipLaunchKernelGGL((decode_merge_kernel<64, true>), dim3(mblocks), dim3(kThreads), 0, st, p);
-    else hipLaunchKernelGGL((decode_merge_kernel<64, false>), dim3(mblocks), dim3(kThreads), 0, st, p);
-  } else {
-    if (a.o_bf16) hipLaunchKernelGGL((decode_merge_kernel<128, true>), dim3(mblocks), dim3(kThreads), 0, st, p);
-    else hipLaunchKernelGGL((decode_merge_kernel<128, false>), dim3(mblocks), dim3(kThreads), 0, st, p);
+  if (fold) {
+    p.n_fold = fold->n;
+    for (int j = 0; j < fold->n; ++j) {
+      p.fold_o[j] = fold->o[j];
+      p.fold_lse[j] = fold->lse[j];
+    }
+    p.own_o = fold->own_o;
+    p.own_lse = fold->own_lse;
   }
+  if (a.d == 64) launch_merge_d<64>(p, a.o_bf16, fold, st);
+  else launch_merge_d<128>(p, a.o_bf16, fold, st);
   return check_launch("cpa_partial_attn_paged (decode merge)");
 }
 

@@ -96,6 +96,19 @@ cpa_status launch_attn_pp(const AttnArgs* shards, int n_shards, bool paged, hipS
                           void* order_ws = nullptr, size_t order_ws_bytes = 0, const MergedOut* merged = nullptr,
                           const AccumIO* accum = nullptr);
 size_t decode_workspace_bytes(int32_t num_seqs, int32_t max_blocks, int32_t block_size, int32_t hq, int32_t d);
-cpa_status launch_attn_decode(const AttnArgs& a, hipStream_t st);
+// With `fold`, the decode merge also folds other ranks' partials (O, LSE) of
+// the same rows into the result: a.o, a.lse receive the exact merge of this
+// rank's partial with fold->o[0..n), and fold->own_o / own_lse (either may be
+// NULL) receive this rank's own partial in the parts' dtype.
+constexpr int kMaxFoldParts = 15;
+struct DecodeFold {
+  int n;
+  const void* o[kMaxFoldParts];
+  const float* lse[kMaxFoldParts];
+  bool part_bf16;
+  void* own_o;
+  float* own_lse;
+};
+cpa_status launch_attn_decode(const AttnArgs& a, hipStream_t st, const DecodeFold* fold = nullptr);
 
 }  // namespace cpa

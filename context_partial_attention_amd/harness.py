@@ -9,7 +9,8 @@ movement, and runs the hot path of each schedule:
   pass_q   one partial of all new queries per rank's paged round-robin shard
            (every rank's pool resident in this GPU's memory), then the merge
   decode   one partial per rank's paged round-robin shard for the single query
-           of every sequence, then the merge
+           of every sequence; the rank's own partial is merged with the other
+           ranks' (resident) partials inside its own decode launches
 
 The CPU oracle never sees anything built here except the raw draws of
 workloads.draw_sequence, which both sides share.
@@ -228,14 +229,39 @@ class Runner:
             fn()
         return graph
 
+    def decode_fold(self, stream=None, own=True):
+        """Decode: the rank's own partial against its paged shard, merged in
+        the same call with the other ranks' partials already in o_parts /
+        lse_parts (self.o, self.lse receive the result). With `own`, the rank's
+        own partial is also written to its o_parts / lse_parts entry."""
+        inp, w = self.inp, self.w
+        r = w.rank
+        others = [i for i in range(w.cp) if i != r]
+        rk = inp["ranks"][r]
+        cpa.partial_attn_paged_merged(inp["q"], inp["q_pos"], inp["cu_q"], rk["k_cache"], rk["v_cache"],
+                                      rk["block_table"], rk["local_kv_lens"], w.cp, rk["rank"], w.interleave,
+                                      inp["max_q"], w.scale, [self.o_parts[i] for i in others],
+                                      [self.lse_parts[i] for i in others], True, out=self.o, lse=self.lse,
+                                      own_out=self.o_parts[r] if own else None,
+                                      own_lse=self.lse_parts[r] if own else None, workspace=self.workspace,
+                                      stream=stream)
+
     def merge(self, stream=None):
         cpa.lse_merge(self.o_parts, self.lse_parts, out=self.o, lse_out=self.lse, stream=stream)
 
     def step(self, stream=None):
         """The rank's whole share: every partial, then the merge. Pass-KV steps
-        run as one batched launch (their shards are all resident)."""
+        run as one batched launch (their shards are all resident); a decode
+        step computes the other ranks' partials (as they would arrive), then
+        the rank's own partial with the merge folded in."""
         if self.w.kind == "pass_kv":
             self.partials_batched(stream)
+        elif self.w.kind == "decode":
+            for i in range(self.w.cp):
+                if i != self.w.rank:
+                    self.partial(i, stream)
+            self.decode_fold(stream)
+            return
         else:
             for i in range(self.w.cp):
                 self.partial(i, stream)

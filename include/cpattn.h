@@ -371,6 +371,48 @@ cpa_status cpa_partial_attn_paged(const void* q, const int32_t* q_pos, const int
                                   size_t workspace_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------
+ * cpa_partial_attn_paged_merged — decode partial attention against this
+ * rank's paged shard, merged in the same call with the other ranks' partials
+ * of the same rows (device).
+ *
+ * [PASSKV], Purpose: in allgather decode every rank attends the gathered
+ * decode queries to its round-robin share of the KV cache and the per-rank
+ * partials are merged exactly. Once the other ranks' partials are resident
+ * (received), this call computes the rank's own partial exactly as
+ * cpa_partial_attn_paged does for max_q == 1 and folds the received ones into
+ * it by the rule of cpa_lse_merge inside the decode kernels' final merge, so
+ * no separate merge launch follows.
+ *
+ * In: every argument of cpa_partial_attn_paged, with max_q <= 1 (decode);
+ *   n_parts in [0, 15]; o_parts and lse_parts are HOST arrays of n_parts
+ *   DEVICE pointers: o_parts[j] [Tq][hq][d] in part_dtype (CPA_F32 or
+ *   CPA_BF16), lse_parts[j] [Tq][hq] natural-log LSE, -inf for a row with no
+ *   visible key (its O is then not read).
+ * Out (device): o [Tq][hq][d] in o_dtype and lse [Tq][hq]: the exact merge of
+ *   this rank's partial with the n_parts partials (O = 0, LSE = -inf where
+ *   every part is empty); own_o [Tq][hq][d] in part_dtype and own_lse
+ *   [Tq][hq] (each may be NULL): this rank's own partial, for the ranks that
+ *   still need it. Rows of sequences without a query are not written.
+ *   Outputs must not overlap the parts.
+ * workspace: as cpa_partial_attn_paged (cpa_partial_attn_paged_workspace).
+ * Errors: as cpa_partial_attn_paged; CPA_ERR_UNSUPPORTED for max_q > 1;
+ *   CPA_ERR_INVALID_ARG for n_parts out of range, NULL part arrays or
+ *   pointers, or a bad part_dtype.
+ * ------------------------------------------------------------------------- */
+cpa_status cpa_partial_attn_paged_merged(const void* q, const int32_t* q_pos, const int32_t* cu_q,
+                                         const void* k_cache, const void* v_cache,
+                                         const int32_t* block_table, int32_t max_blocks,
+                                         const int32_t* local_kv_lens, int32_t block_size,
+                                         int32_t cp_size, int32_t cp_rank, int32_t interleave,
+                                         int32_t num_seqs, int32_t max_q, int32_t hq, int32_t hkv,
+                                         int32_t d, cpa_dtype in_dtype, float scale, cpa_mask mask,
+                                         int32_t n_parts, const void* const* o_parts,
+                                         const float* const* lse_parts, cpa_dtype part_dtype,
+                                         void* own_o, float* own_lse, void* o, cpa_dtype o_dtype,
+                                         float* lse, void* workspace, size_t workspace_bytes,
+                                         void* stream);
+
+/* ---------------------------------------------------------------------------
  * cpa_lse_merge — exact n-way merge of partial (O, LSE) results (device).
  *
  * The partials come from disjoint key sets (the KV shards of the ranks), so

@@ -192,6 +192,24 @@ def test_merged_call_validation_before_gpu(cpa):
     assert merged(2, dt=1) == -2  # fp32 inputs: no merged walk
 
 
+def test_paged_merged_call_validation_before_gpu(cpa):
+    lib = cpa.load_library()
+    fake = ctypes.c_void_p(0x1000)  # never dereferenced: validation fails first
+    arr = (ctypes.c_void_p * 16)(*([0x1000] * 16))
+
+    def call(maxq=1, n=1, parts=arr, pdt=0, ws=fake, wsb=1 << 20, bs=16, rank=0):
+        return lib.cpa_partial_attn_paged_merged(fake, fake, fake, fake, fake, fake, 8, fake, bs, 2, rank, 8, 2, maxq,
+                                                 8, 2, 128, 0, 0.1, 1, n, parts, parts, pdt, None, None, fake, 0,
+                                                 fake, ws, wsb, None)
+
+    assert call(maxq=4) == -2  # decode only
+    assert call(n=16) == -1 and call(n=-1) == -1  # part count out of range
+    assert call(parts=None) == -1  # NULL part arrays
+    assert call(pdt=5) == -1  # bad part dtype
+    assert call(ws=None, wsb=0) == -3  # decode workspace missing
+    assert call(bs=32) == -2 and call(rank=2) == -1  # the paged checks
+
+
 def test_choose_pass_matches_oracle(cpa):
     """Host choice of the exchanged shard: bit-exact against the oracle on
     random batches, and the pages' two cases."""

@@ -93,6 +93,26 @@ def test_paged_checks_cache_table_and_lengths():
             table, lens, 2, 0, 8, 3, 0.125)
 
 
+def test_paged_merged_checks_the_received_parts():
+    tq, hq, hkv, d = 2, 4, 2, 64
+    q = torch.zeros((tq, hq, d), dtype=torch.bfloat16)
+    q_pos = torch.tensor([29, 39], dtype=torch.int32)
+    cu_q = torch.tensor([0, 1, 2], dtype=torch.int32)
+    kc = torch.zeros((8, hkv, 16, d), dtype=torch.bfloat16)
+    table = torch.zeros((2, 4), dtype=torch.int32)
+    lens = torch.tensor([15, 20], dtype=torch.int32)
+    o1, l1 = torch.zeros((tq, hq, d)), torch.zeros((tq, hq))
+    head = (q, q_pos, cu_q, kc, kc.clone(), table, lens, 2, 0, 8)
+    f = cpa.partial_attn_paged_merged
+    _raises("must be a GPU tensor", f, *head, 1, 0.125, [o1], [l1])
+    _raises("decode", f, *head, 3, 0.125, [o1], [l1])
+    _raises("same number", f, *head, 1, 0.125, [o1, o1], [l1])
+    _raises(r"o_parts\[1\] has dtype", f, *head, 1, 0.125, [o1, o1.bfloat16()], [l1, l1])
+    _raises(r"lse_parts\[0\] has shape", f, *head, 1, 0.125, [o1], [l1[:1]])
+    _raises("own_out has dtype", f, *head, 1, 0.125, [o1], [l1], own_out=o1.bfloat16())
+    _raises("block_table has dtype", f, q, q_pos, cu_q, kc, kc, table.long(), lens, 2, 0, 8, 1, 0.125, [o1], [l1])
+
+
 def test_lse_merge_checks_parts_and_outputs():
     o = torch.zeros((5, 4, 64))
     l = torch.zeros((5, 4))

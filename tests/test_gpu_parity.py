@@ -121,6 +121,75 @@ def test_small_bf16_all_elements(cpa, wl, harness, name, changes):
     _check_schedule(harness, w, pool_fill=float("nan"))
 
 
+FOLD_CASES = [
+    # sequences shorter than one interleave group: the other rank has no key for them (LSE -inf)
+    ("decode_fold_cp2_short", dict(kind="decode", batch=7, lengths=(1, 5, 8, 9, 17, 100, 3000), len_range=(), cp=2,
+                                   rank=0, interleave=8)),
+    ("decode_fold_cp4_d64_g8", dict(kind="decode", batch=9, len_range=(1, 700), lengths=(), cp=4, rank=2,
+                                    interleave=3, d=64, hq=16, hkv=2)),
+]
+
+
+@pytest.mark.parametrize("name,changes", FOLD_CASES, ids=[c[0] for c in FOLD_CASES])
+def test_decode_fold_all_elements(cpa, wl, harness, name, changes):
+    """Decode with the other ranks' partials folded into the rank's own decode
+    launches: every element against the oracle's merge of all ranks, within
+    1e-5 of the separate merge of the same partials, the rank's own partial
+    bit-identical to the plain decode call, received rows with LSE -inf never
+    read (their O is NaN), bf16 parts, and no parts at all."""
+    w = wl.scaled(wl.WORKLOADS["allgather_decode_cp2"], name=name, seed=300 + len(name), **changes)
+    _say(f"case {name}")
+    nan = float("nan")
+    inp = harness.build(w, device="cuda", pool_fill=nan)
+    run = harness.Runner(inp, merged_dtype=torch.float32)
+    run.poison()
+    r = w.rank
+    others = [i for i in range(w.cp) if i != r]
+    for i in range(w.cp):
+        run.partial(i)
+    run.merge()
+    torch.cuda.synchronize()
+    sep_o, sep_l = run.o.clone(), run.lse.clone()
+    own_o, own_l = run.o_parts[r].clone(), run.lse_parts[r].clone()
+    _, parts, merged = expected_round_robin(inp, None)
+    n_empty = 0
+    for i in others:
+        empty = torch.isneginf(run.lse_parts[i])
+        n_empty += int(empty.sum())
+        run.o_parts[i][empty] = nan
+    if name.endswith("short"):
+        assert n_empty > 0
+    for t in (run.o, run.lse, run.o_parts[r], run.lse_parts[r]):
+        t.fill_(nan)
+    run.decode_fold()
+    torch.cuda.synchronize()
+    assert torch.equal(run.o_parts[r], own_o) and torch.equal(run.lse_parts[r], own_l)
+    e = assert_close(f64(run.o), f64(run.lse), merged[0], merged[1], f"{name} folded")
+    _say(f"  folded: max|dO|={e[0]:.2e} max|dLSE|={e[1]:.2e}")
+    np.testing.assert_allclose(f64(run.o), f64(sep_o), rtol=0, atol=1e-5)
+    np.testing.assert_allclose(f64(run.lse), f64(sep_l), rtol=0, atol=1e-5)
+
+    # parts received in bf16, result in bf16
+    rk = inp["ranks"][r]
+    args = (inp["q"], inp["q_pos"], inp["cu_q"], rk["k_cache"], rk["v_cache"], rk["block_table"],
+            rk["local_kv_lens"], w.cp, r, w.interleave, inp["max_q"], w.scale)
+    bparts = [run.o_parts[i].bfloat16() for i in others]
+    own_b = torch.full_like(bparts[0], nan)
+    ob, lb = cpa.partial_attn_paged_merged(*args, bparts, [run.lse_parts[i] for i in others],
+                                           out_dtype=torch.bfloat16, own_out=own_b)
+    torch.cuda.synchronize()
+    assert torch.equal(own_b, own_o.bfloat16())
+    # (the received rows holding NaN have LSE -inf, hence weight 0: zeros stand in for them)
+    ref_o, ref_l = oracle.lse_merge([f64(own_o)] + [np.nan_to_num(f64(b), nan=0.0) for b in bparts],
+                                    [f64(own_l)] + [f64(run.lse_parts[i]) for i in others])
+    assert_close(f64(ob), f64(lb), ref_o, ref_l, f"{name} bf16 parts")
+
+    # no received parts: the plain decode call's result, bit for bit
+    o0, l0 = cpa.partial_attn_paged_merged(*args, [], [])
+    torch.cuda.synchronize()
+    assert torch.equal(o0, own_o) and torch.equal(l0, own_l)
+
+
 def test_small_bf16_output_and_no_mask(cpa, wl, harness):
     w = wl.scaled(wl.WORKLOADS["qwen2.5_3b_cp2_rank0"], name="nomask", lengths=(400, 129), batch=2, len_range=())
     _say("case bf16 output + no mask")
