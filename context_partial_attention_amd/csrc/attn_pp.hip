@@ -497,7 +497,9 @@ __global__ __launch_bounds__(kThreads, 1) void attn_pp_kernel(PPParams p) {
       }
       if (ph & 1) {
         if (t_ld + 1 <= n) store_slot(t_ld + 1);
-        lds_barrier();
+        // the last phase publishes no slot and no LDS is read after it, so
+        // group 0 goes on to its epilogue while group 1 runs its last PV
+        if (ph < 2 * n + 1) lds_barrier();
       }
     }
   }
