@@ -201,14 +201,21 @@ class Runner:
                                 workspace=self.workspace, stream=stream)
 
     def ring_accumulate(self, stream=None, out=None):
-        """The pass-KV steps as a ring would run them: one shard at a time, each
-        folded into the running (o_parts[0], lse_parts[0]) (fp32); `out` (or
-        self.o) receives the merged O at the last step, self.lse the LSE."""
+        """The pass-KV steps as a ring would run them: one shard at a time. The
+        rank's own shard (step 0) is a plain partial into (o_parts[0],
+        lse_parts[0]) (fp32); every later shard is folded into that running
+        (O, LSE) as it arrives. `out` (or self.o) receives the merged O at the
+        last step, self.lse the LSE."""
         inp, w = self.inp, self.w
         o_acc, lse_acc = self.o_parts[0], self.lse_parts[0]
-        lse_acc.fill_(float("-inf"))
         for i, st in enumerate(inp["steps"]):
             last = i == len(inp["steps"]) - 1
+            if i == 0:
+                cpa.partial_attn(inp["q"], inp["q_pos"], inp["cu_q"], st["k"], st["v"], st["k_pos"], st["cu_k"],
+                                 inp["max_q"], w.scale, True, out=o_acc, lse=lse_acc, stream=stream)
+                if last:  # a single shard: the partial is the result
+                    (self.o if out is None else out).copy_(o_acc)
+                continue
             cpa.partial_attn_accumulate(inp["q"], inp["q_pos"], inp["cu_q"], st["k"], st["v"], st["k_pos"],
                                         st["cu_k"], inp["max_q"], w.scale, o_acc, lse_acc,
                                         out=(self.o if out is None else out) if last else None, stream=stream)

@@ -401,27 +401,28 @@ def test_merged_walk_unsupported_cases(cpa, wl, harness):
 @pytest.mark.parametrize("name,changes", MERGED, ids=[m[0] for m in MERGED])
 def test_ring_accumulate_all_elements(cpa, wl, harness, name, changes):
     """Running merge: the shards folded in one at a time into (O, LSE) equal
-    the oracle's merged result; an accumulator row with LSE -inf is never
-    read (it holds NaN here); starting from a plain partial gives the same."""
+    the oracle's merged result, both as the ring runs them (the own shard as
+    a plain partial, the others folded in) and folded into an empty
+    accumulator (LSE -inf, O NaN: an empty row's O is never read)."""
     w = wl.scaled(wl.WORKLOADS["qwen2.5_3b_cp2_rank0"], name=name, seed=600 + len(name), **changes)
     _say(f"case ring {name}")
     inp = harness.build(w, device="cuda")
     run = harness.Runner(inp)
     _, _, merged = expected_pass_kv(inp, None)
-    run.o_parts[0].fill_(float("nan"))
+    run.poison()
     run.ring_accumulate()
     torch.cuda.synchronize()
     assert_close(f64(run.o), f64(run.lse), merged[0], merged[1], f"ring {name} (bf16 out)")
     assert_close(f64(run.o_parts[0]), f64(run.lse_parts[0]), merged[0], merged[1], f"ring {name} (fp32 acc)")
-    # first step as a plain partial into the accumulator, the rest folded in
+    # every shard folded into an empty accumulator
     st = inp["steps"]
-    o_acc, lse_acc = cpa.partial_attn(inp["q"], inp["q_pos"], inp["cu_q"], st[0]["k"], st[0]["v"], st[0]["k_pos"],
-                                      st[0]["cu_k"], inp["max_q"], w.scale, True)
-    for s in st[1:]:
+    o_acc = torch.full_like(run.o_parts[0], float("nan"))
+    lse_acc = torch.full_like(run.lse_parts[0], float("-inf"))
+    for s in st:
         cpa.partial_attn_accumulate(inp["q"], inp["q_pos"], inp["cu_q"], s["k"], s["v"], s["k_pos"], s["cu_k"],
                                     inp["max_q"], w.scale, o_acc, lse_acc)
     torch.cuda.synchronize()
-    assert_close(f64(o_acc), f64(lse_acc), merged[0], merged[1], f"ring {name} from a partial")
+    assert_close(f64(o_acc), f64(lse_acc), merged[0], merged[1], f"ring {name} from an empty accumulator")
 
 
 GRAPH_CASES = [
