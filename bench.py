@@ -38,7 +38,7 @@ DEFAULT_WORKLOADS = [HEADLINE, "qwen2.5_3b_cp2_rank0", "chunked_prefill_passq_cp
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0  # MI355X HBM3E
 # dominant kernel of the headline step and the committed counter summary of it
-ATTN_KERNEL_SOURCES = ("attn_pp.hip", "device_common.h")
+ATTN_KERNEL_SOURCES = ("attn_pp.hip", "attn_pp_common.h", "device_common.h")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_llama3_8b_128k_traffic.md")
 
 
