@@ -90,7 +90,7 @@ def load_library():
                                             _i32, _f32, _i32, _p, _i32, _p, _p, ctypes.c_size_t, _p]
     lib.cpa_partial_attn_accumulate.restype = _i32
     lib.cpa_partial_attn_accumulate.argtypes = [_p, _p, _p, _p, _p, _p, _p, _i32, _i32, _i32, _i32, _i32, _i32, _f32,
-                                                _i32, _p, _p, _p, _i32, _p]
+                                                _i32, _p, _p, _p, _i32, _p, ctypes.c_size_t, _p]
     lib.cpa_partial_attn_paged_workspace.restype = _i32
     lib.cpa_partial_attn_paged_workspace.argtypes = [_i32, _i32, _i32, _i32, _i32, _i32,
                                                      ctypes.POINTER(ctypes.c_size_t)]
@@ -437,9 +437,11 @@ def partial_attn_merged(q, q_pos, cu_q, ks, vs, k_poss, cu_ks, max_q: int, scale
 
 
 def partial_attn_accumulate(q, q_pos, cu_q, k, v, k_pos, cu_k, max_q: int, scale: float, o_acc, lse_acc,
-                            causal: bool = True, out=None, stream=None):
+                            causal: bool = True, out=None, workspace=None, stream=None):
     """One pass-KV step folded into the running (o_acc, lse_acc) (fp32, in place); `out`, if given,
-    also receives the merged O (bf16 or fp32). Returns (o_acc, lse_acc)."""
+    also receives the merged O (bf16 or fp32). `workspace` (a uint8 GPU tensor of at least
+    partial_attn_multi_workspace(1, ...) bytes, or None) enables the heaviest-first launch order.
+    Returns (o_acc, lse_acc)."""
     torch = _torch()
     tq, hq, d = _check_q(q)
     hkv = _check_kv(q, k, v)
@@ -451,13 +453,15 @@ def partial_attn_accumulate(q, q_pos, cu_q, k, v, k_pos, cu_k, max_q: int, scale
     _shape(lse_acc, "lse_acc", (tq, hq), torch.float32)
     if out is not None:
         _shape(out, "out", (tq, hq, d), (torch.float32, torch.bfloat16))
+    _check_workspace(workspace)
     _same_device(("q", q), ("q_pos", q_pos), ("cu_q", cu_q), ("k", k), ("v", v), ("k_pos", k_pos), ("cu_k", cu_k),
-                 ("o_acc", o_acc), ("lse_acc", lse_acc), ("out", out))
+                 ("o_acc", o_acc), ("lse_acc", lse_acc), ("out", out), ("workspace", workspace))
     _check("cpa_partial_attn_accumulate", load_library().cpa_partial_attn_accumulate(
         _dev(q, "q"), _dev(q_pos, "q_pos"), _dev(cu_q, "cu_q"), _dev(k, "k"), _dev(v, "v"), _dev(k_pos, "k_pos"),
         _dev(cu_k, "cu_k"), num_seqs, int(max_q), hq, hkv, d, _dtype_code(q), float(scale),
         MASK_CAUSAL if causal else MASK_NONE, _dev(o_acc, "o_acc"), _dev(lse_acc, "lse_acc"), _dev(out, "out"),
-        F32 if out is None else _dtype_code(out), _stream(stream)))
+        F32 if out is None else _dtype_code(out), _dev(workspace, "workspace"),
+        0 if workspace is None else workspace.numel() * workspace.element_size(), _stream(stream)))
     return o_acc, lse_acc
 
 

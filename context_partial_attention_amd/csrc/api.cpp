@@ -239,7 +239,8 @@ extern "C" cpa_status cpa_partial_attn_accumulate(const void* q, const int32_t* 
                                                   const int32_t* cu_k, int32_t num_seqs, int32_t max_q, int32_t hq,
                                                   int32_t hkv, int32_t d, cpa_dtype in_dtype, float scale,
                                                   cpa_mask mask, float* o_acc, float* lse_acc, void* o_out,
-                                                  cpa_dtype o_out_dtype, void* stream) {
+                                                  cpa_dtype o_out_dtype, void* workspace, size_t workspace_bytes,
+                                                  void* stream) {
   const char* fn = "cpa_partial_attn_accumulate";
   if (in_dtype != CPA_BF16 && in_dtype != CPA_F32) return fail(CPA_ERR_INVALID_ARG, "%s: bad in_dtype", fn);
   if (o_out_dtype != CPA_BF16 && o_out_dtype != CPA_F32) return fail(CPA_ERR_INVALID_ARG, "%s: bad o_out_dtype", fn);
@@ -273,7 +274,7 @@ extern "C" cpa_status cpa_partial_attn_accumulate(const void* q, const int32_t* 
   if (st != CPA_OK) return st;
   if (num_seqs == 0 || max_q == 0) return CPA_OK;
   const AccumIO io{o_acc, lse_acc, o_out};
-  return launch_attn_pp(&a, 1, /*paged=*/false, (hipStream_t)stream, nullptr, 0, nullptr, &io);
+  return launch_attn_pp(&a, 1, /*paged=*/false, (hipStream_t)stream, workspace, workspace_bytes, nullptr, &io);
 }
 
 extern "C" cpa_status cpa_partial_attn_paged_workspace(int32_t num_seqs, int32_t max_q, int32_t max_blocks,

@@ -210,15 +210,17 @@ class Runner:
         o_acc, lse_acc = self.o_parts[0], self.lse_parts[0]
         for i, st in enumerate(inp["steps"]):
             last = i == len(inp["steps"]) - 1
-            if i == 0:
-                cpa.partial_attn(inp["q"], inp["q_pos"], inp["cu_q"], st["k"], st["v"], st["k_pos"], st["cu_k"],
-                                 inp["max_q"], w.scale, True, out=o_acc, lse=lse_acc, stream=stream)
+            if i == 0:  # heaviest-first order through the one-shard batched call
+                cpa.partial_attn_multi(inp["q"], inp["q_pos"], inp["cu_q"], [st["k"]], [st["v"]], [st["k_pos"]],
+                                       [st["cu_k"]], inp["max_q"], w.scale, True, outs=[o_acc], lses=[lse_acc],
+                                       workspace=self.workspace, stream=stream)
                 if last:  # a single shard: the partial is the result
                     (self.o if out is None else out).copy_(o_acc)
                 continue
             cpa.partial_attn_accumulate(inp["q"], inp["q_pos"], inp["cu_q"], st["k"], st["v"], st["k_pos"],
                                         st["cu_k"], inp["max_q"], w.scale, o_acc, lse_acc,
-                                        out=(self.o if out is None else out) if last else None, stream=stream)
+                                        out=(self.o if out is None else out) if last else None,
+                                        workspace=self.workspace, stream=stream)
         self.lse.copy_(lse_acc)
 
     def capture(self, fn=None):

@@ -314,7 +314,10 @@ cpa_status cpa_partial_attn_merged(int32_t n_shards, const void* q, const int32_
  *   earlier steps; a row with lse_acc = -inf counts as empty and its o_acc is
  *   not read (start a ring with lse_acc = -inf, or with a cpa_partial_attn
  *   result in fp32). o_out (device, may be NULL) also receives the merged O
- *   in o_out_dtype (for the last step, say).
+ *   in o_out_dtype (for the last step, say). workspace (device, optional):
+ *   cpa_partial_attn_multi_workspace(1, num_seqs, max_q) bytes for the
+ *   heaviest-first launch order, as in cpa_partial_attn_multi (NULL or short:
+ *   index order, same results).
  * Supported: in_dtype CPA_BF16 with an even GQA group; anything else is
  *   CPA_ERR_UNSUPPORTED.
  * Errors: as cpa_partial_attn; CPA_ERR_INVALID_ARG for NULL o_acc / lse_acc.
@@ -324,7 +327,8 @@ cpa_status cpa_partial_attn_accumulate(const void* q, const int32_t* q_pos, cons
                                        const int32_t* cu_k, int32_t num_seqs, int32_t max_q,
                                        int32_t hq, int32_t hkv, int32_t d, cpa_dtype in_dtype,
                                        float scale, cpa_mask mask, float* o_acc, float* lse_acc,
-                                       void* o_out, cpa_dtype o_out_dtype, void* stream);
+                                       void* o_out, cpa_dtype o_out_dtype, void* workspace,
+                                       size_t workspace_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------
  * cpa_partial_attn_paged_workspace — bytes of device workspace that

@@ -245,7 +245,7 @@ def test_accumulate_call_validation_before_gpu(cpa):
 
     def acc(o_acc=fake, lse_acc=fake, hkv=2, dt=0):
         return lib.cpa_partial_attn_accumulate(fake, fake, fake, fake, fake, fake, fake, 1, 4, 8, hkv, 128, dt, 0.1,
-                                               1, o_acc, lse_acc, None, 0, None)
+                                               1, o_acc, lse_acc, None, 0, None, 0, None)
 
     assert acc(o_acc=None) == -1 and acc(lse_acc=None) == -1  # NULL accumulator
     assert acc(hkv=3) == -1  # hq not a multiple of hkv

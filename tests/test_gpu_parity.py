@@ -416,13 +416,18 @@ def test_ring_accumulate_all_elements(cpa, wl, harness, name, changes):
     assert_close(f64(run.o_parts[0]), f64(run.lse_parts[0]), merged[0], merged[1], f"ring {name} (fp32 acc)")
     # every shard folded into an empty accumulator
     st = inp["steps"]
-    o_acc = torch.full_like(run.o_parts[0], float("nan"))
-    lse_acc = torch.full_like(run.lse_parts[0], float("-inf"))
-    for s in st:
-        cpa.partial_attn_accumulate(inp["q"], inp["q_pos"], inp["cu_q"], s["k"], s["v"], s["k_pos"], s["cu_k"],
-                                    inp["max_q"], w.scale, o_acc, lse_acc)
-    torch.cuda.synchronize()
+    accs = []
+    for ws in (None, run.workspace):  # index order, then heaviest-first order: the same bits
+        o_acc = torch.full_like(run.o_parts[0], float("nan"))
+        lse_acc = torch.full_like(run.lse_parts[0], float("-inf"))
+        for s in st:
+            cpa.partial_attn_accumulate(inp["q"], inp["q_pos"], inp["cu_q"], s["k"], s["v"], s["k_pos"], s["cu_k"],
+                                        inp["max_q"], w.scale, o_acc, lse_acc, workspace=ws)
+        torch.cuda.synchronize()
+        accs.append((o_acc, lse_acc))
+    o_acc, lse_acc = accs[0]
     assert_close(f64(o_acc), f64(lse_acc), merged[0], merged[1], f"ring {name} from an empty accumulator")
+    assert torch.equal(accs[1][0], o_acc) and torch.equal(accs[1][1], lse_acc)
 
 
 GRAPH_CASES = [
