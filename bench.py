@@ -40,6 +40,7 @@ PEAK_HBM_GBS = 8000.0  # MI355X HBM3E
 # dominant kernel of the headline step and the committed counter summary of it
 ATTN_KERNEL_SOURCES = ("attn_pp.hip", "attn_pp_common.h", "device_common.h")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_llama3_8b_128k_traffic.md")
+COUNTERS_FILE = os.path.join(ROOT, "profiles", "attn_llama3_8b_128k_counters.md")
 
 
 def log(msg: str):
@@ -313,6 +314,23 @@ def committed_traffic():
         return None
 
 
+def committed_clock():
+    """Shader clock (GHz) during the headline launch, from the committed
+    rocprofv3 counter summary (GRBM_GUI_ACTIVE per XCC over the traced launch
+    time); None when it is missing or was taken from a different kernel
+    source. The clock a run holds under sustained matrix load varies from box
+    to box, so this is context for the roofline fraction, not a measurement of
+    this run."""
+    if not os.path.exists(COUNTERS_FILE):
+        return None
+    text = open(COUNTERS_FILE).read()
+    dig = re.search(r"kernel_source_digest: `([0-9a-f]+)`", text)
+    clk = re.search(r"shader clock during the launch = .* = ([0-9.]+) GHz", text)
+    if not dig or dig.group(1) != _source_digest() or not clk:
+        return None
+    return float(clk.group(1))
+
+
 # ------------------------------------------------------------------ CPU baseline (oracle)
 
 
@@ -386,11 +404,9 @@ def cpu_baseline(name: str, budget_s: float = 15.0, block_rows: int = 64) -> dic
 
 
 def environment() -> dict:
-    """Software versions, device, and the shader and memory clock levels the
-    driver lists as current in sysfs (read as files: no helper program is
-    started from this GPU process)."""
-    import glob
-
+    """Software versions and the device. (The clock levels the driver lists
+    in sysfs after a run are not the clock the work ran at; the roofline
+    carries the clock measured by the committed counters instead.)"""
     import torch
 
     props = torch.cuda.get_device_properties(0)
@@ -402,15 +418,6 @@ def environment() -> dict:
         "compute_units": props.multi_processor_count,
         "host_cpus": len(os.sched_getaffinity(0)),
     }
-    clocks = {}
-    for path in sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_[sm]clk")):
-        try:
-            with open(path) as f:
-                cur = [ln.split(":", 1)[1].strip().rstrip("*").strip() for ln in f if ln.rstrip().endswith("*")]
-            clocks[path.split("/")[4] + "/" + path.rsplit("_", 1)[1]] = cur[0] if cur else None
-        except (OSError, IndexError):
-            continue
-    env["clocks_current_level"] = clocks or None
     try:
         with open("/opt/rocm/.info/version") as f:
             env["rocm"] = f.read().strip()
@@ -469,6 +476,7 @@ def main():
     flops_per_launch = h["flops_per_step"] / len(h["partial_ms"])
     achieved = flops_per_launch / (part_ms * 1e-3) / 1e12
     traffic = committed_traffic()
+    clock = committed_clock()
     line = {
         "metric": METRIC,
         "value": h["TFLOPs"],
@@ -505,6 +513,11 @@ def main():
             "traffic": traffic,
             "avg_launch_ms": part_ms,
             "flops_per_launch": flops_per_launch,
+            # from the committed counters (same kernel source), not this run:
+            # the shader clock under this launch's load and the dense bf16 rate
+            # of 1024 SIMDs x 1024 FLOP per clock at that clock
+            "profiled_shader_clock_ghz": clock,
+            "mfma_peak_at_profiled_clock": 1024 * 1024 * clock * 1e-3 if clock else None,
         },
         "workloads": {k: v for k, v in results.items() if k != HEADLINE},
         # not the step above: the fused-merge walk (cpa_partial_attn_merged) on
