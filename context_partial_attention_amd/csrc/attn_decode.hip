@@ -285,11 +285,26 @@ __global__ __launch_bounds__(kThreads) void decode_merge_kernel(DecParams p) {
     float sum = 0.f;
     for (int s = lane; s < n_splits; s += 64) sum += hw_exp2(p.ws_lse[slot0 + s] - mx);
     lse2 = mx + hw_log2(wave_sum(sum));
-    for (int s = 0; s < n_splits; ++s) {
-      const float w = hw_exp2(p.ws_lse[slot0 + s] - lse2);
-      const float* src = p.ws_o + (slot0 + s) * D;
+    // 8 splits' reads issued before their sums (one round trip per 8 splits
+    // instead of one per split); the sums stay in split order. Reads past the
+    // last split repeat it and get weight 0.
+    constexpr int kU = 8;
+    for (int s0 = 0; s0 < n_splits; s0 += kU) {
+      float lv[kU], x[kU][kPer];
 #pragma unroll
-      for (int i = 0; i < kPer; ++i) acc[i] = fmaf(w, src[lane + 64 * i], acc[i]);
+      for (int u = 0; u < kU; ++u) {
+        const int s = min(s0 + u, n_splits - 1);
+        lv[u] = p.ws_lse[slot0 + s];
+        const float* src = p.ws_o + (slot0 + s) * D;
+#pragma unroll
+        for (int i = 0; i < kPer; ++i) x[u][i] = src[lane + 64 * i];
+      }
+#pragma unroll
+      for (int u = 0; u < kU; ++u) {
+        const float w = s0 + u < n_splits ? hw_exp2(lv[u] - lse2) : 0.f;
+#pragma unroll
+        for (int i = 0; i < kPer; ++i) acc[i] = fmaf(w, x[u][i], acc[i]);
+      }
     }
   }
   if constexpr (FOLD) {

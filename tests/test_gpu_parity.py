@@ -189,6 +189,21 @@ def test_decode_fold_all_elements(cpa, wl, harness, name, changes):
     torch.cuda.synchronize()
     assert torch.equal(o0, own_o) and torch.equal(l0, own_l)
 
+    # the most parts the call takes (15): random partials beside the received ones, some rows empty
+    g = torch.Generator(device="cuda").manual_seed(17)
+    extra = 15 - len(others)
+    xo = [torch.randn(own_o.shape, device="cuda", generator=g) for _ in range(extra)]
+    xl = [torch.randn(own_l.shape, device="cuda", generator=g) * 4 for _ in range(extra)]
+    for t in xl:
+        t[torch.rand(t.shape, device="cuda", generator=g) < 0.2] = float("-inf")
+    po = [run.o_parts[i] for i in others] + xo
+    pl = [run.lse_parts[i] for i in others] + xl
+    om, lm = cpa.partial_attn_paged_merged(*args, po, pl)
+    torch.cuda.synchronize()
+    ref_o, ref_l = oracle.lse_merge([f64(own_o)] + [np.nan_to_num(f64(t), nan=0.0) for t in po],
+                                    [f64(own_l)] + [f64(t) for t in pl])
+    assert_close(f64(om), f64(lm), ref_o, ref_l, f"{name} 15 parts")
+
 
 def test_small_bf16_output_and_no_mask(cpa, wl, harness):
     w = wl.scaled(wl.WORKLOADS["qwen2.5_3b_cp2_rank0"], name="nomask", lengths=(400, 129), batch=2, len_range=())
