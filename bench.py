@@ -4,8 +4,9 @@ python bench.py [--gpus 1] [--steps K] [--warmup W] [--workloads a,b,...] [--no-
 
 A step is one CP rank's whole share of one batch: every partial attention the
 rank computes, then the merge of all partials (other ranks' partials already
-resident in HBM where the schedule has them). Inputs are seeded synthetic
-tensors resident in HBM before timing starts.
+resident in HBM where the schedule has them; in decode the merge is folded
+into the rank's own decode launches). Inputs are seeded synthetic tensors
+resident in HBM before timing starts.
 
 Headline (`value`): the largest workload, the Llama-3-8B-shaped 128K-token
 cp=4 rank-1 pass-KV share (1 sequence of 131072 tokens, zigzag into 8 chunks,
