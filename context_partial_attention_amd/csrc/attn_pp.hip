@@ -171,6 +171,21 @@ __global__ __launch_bounds__(kThreads, 1) void attn_pp_kernel(PPParams p) {
     }
     __syncthreads();
   }
+  // Tiles t < n_fast need no position read in the matrix phase: every key of
+  // them is visible to every row of the workgroup. A shard's key positions
+  // increase strictly, and tile t+3 < n starts at or below blk_qmax, so tile
+  // t ends below blk_qmax - 128; when the workgroup's rows hold consecutive
+  // positions (the first at blk_qmax - (blk_last - row0)), that is below every
+  // row's position. (Not for a walk over several shards, whose positions do
+  // not increase across shards.)
+  int n_fast = 0;
+  if constexpr (!MERGED) {
+    if (!p.causal) {
+      n_fast = max(0, n - 1);  // only a partial last tile has masked keys
+    } else if (blk_qmax - p.q_pos[row0] == blk_last - row0) {
+      n_fast = max(0, n - 3);
+    }
+  }
   // tile t of the walk: its shard's K, V and positions, first key index, end of the visible keys
   struct TileRef {
     const uint16_t* k;
@@ -350,7 +365,8 @@ __global__ __launch_bounds__(kThreads, 1) void attn_pp_kernel(PPParams p) {
     __builtin_amdgcn_s_setprio(2);
     const int s = t & 1;
     const bool do_pv = t >= 1 && p_valid;
-    const bool do_qk = t < n && __builtin_amdgcn_readfirstlane(kpos_sh[t & 3][0]) <= wave_qmax;
+    const bool do_qk =
+        t < n && (t < n_fast ? wave_active : __builtin_amdgcn_readfirstlane(kpos_sh[t & 3][0]) <= wave_qmax);
     b_valid = do_qk;  // B(t) has work iff some key of tile t is visible to this wave
     const uint16_t* vs = vslot(s);
     const uint16_t* ks = kslot(s);
@@ -438,7 +454,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_pp_kernel(PPParams p) {
   // than as the first (dependent) LDS reads of the softmax phase
   auto phase_a = [&](int t) {
     phase_a_body(t);
-    b_mask = b_valid && __builtin_amdgcn_readfirstlane(kpos_sh[t & 3][kBN - 1]) > wave_qmin;
+    b_mask = b_valid && t >= n_fast && __builtin_amdgcn_readfirstlane(kpos_sh[t & 3][kBN - 1]) > wave_qmin;
   };
 
   // B(t): mask and online softmax of S(t) -> P(t) (fp32, in place)
