@@ -103,16 +103,16 @@ def bench_workload(name: str, steps: int, warmup: int, next_rows: bool = True) -
         for r in range(w.cp):
             if r != w.rank:
                 run.partial(r)
-        if w.kind == "decode":
-            # decode: the received partials are merged inside the rank's own
-            # decode launches (split kernel + merge kernel), no merge launch;
-            # the rank's own partial is written once, for the separate merge
-            # timed below for comparison
-            run.partial(w.rank)
-            launches = [lambda: run.decode_fold(own=False)]
+        # the received partials are merged inside the rank's own launches
+        # (decode: split kernel + merge kernel; pass-Q: the prefill kernel's
+        # epilogue), no merge launch; the rank's own partial is written once,
+        # for the separate merge timed below for comparison
+        run.partial(w.rank)
+        if run.fold_supported():
+            launches = [lambda: run.rank_fold(own=False)]
         else:
             launches = [lambda: run.partial(w.rank)]
-    merge_in_step = w.kind != "decode"
+    merge_in_step = w.kind == "pass_kv" or not run.fold_supported()
 
     def step():
         for f in launches:
@@ -253,6 +253,7 @@ def bench_workload(name: str, steps: int, warmup: int, next_rows: bool = True) -
         res["partial_cold_hbm_frac"] = res["partial_cold_GBps"] / PEAK_HBM_GBS
         res["GBps"] = step_bytes / (res["ms_per_step"] * 1e-3) / 1e9
         res["hbm_frac"] = res["GBps"] / PEAK_HBM_GBS
+    if not merge_in_step:
         # the separate cp-way merge launch the fold replaces, timed on its own
         # for comparison (not part of the step)
         for k in [k for k in res if k.startswith("merge_")]:

@@ -528,16 +528,15 @@ def partial_attn_paged_merged(q, q_pos, cu_q, k_cache, v_cache, block_table, loc
                               cp_rank: int, interleave: int, max_q: int, scale: float, o_parts, lse_parts,
                               causal: bool = True, out=None, lse=None, out_dtype=None, own_out=None, own_lse=None,
                               workspace=None, stream=None):
-    """Decode (max_q <= 1): this rank's partial against its paged shard, merged
-    in the same call with the other ranks' partials o_parts[j] [Tq,hq,d],
-    lse_parts[j] [Tq,hq]. own_out / own_lse (optional) receive this rank's own
-    partial in the parts' dtype. Returns (o, lse)."""
+    """This rank's partial against its paged shard (decode, or pass-Q prefill
+    with an even GQA group), merged in the same call with the other ranks'
+    partials o_parts[j] [Tq,hq,d], lse_parts[j] [Tq,hq]. own_out / own_lse
+    (optional) receive this rank's own partial in the parts' dtype. Returns
+    (o, lse)."""
     torch = _torch()
     tq, hq, d = _check_q(q)
     num_seqs, hkv, block_size, max_blocks = _check_paged(q, q_pos, cu_q, k_cache, v_cache, block_table,
                                                          local_kv_lens, causal)
-    if int(max_q) > 1:
-        raise ValueError(f"partial_attn_paged_merged is for decode (max_q <= 1), got max_q = {max_q}")
     n = len(o_parts)
     if n != len(lse_parts) or n > 15:
         raise ValueError("need the same number (at most 15) of O and LSE parts")

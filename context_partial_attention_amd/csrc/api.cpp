@@ -377,7 +377,6 @@ extern "C" cpa_status cpa_partial_attn_paged_merged(
     const float* const* lse_parts, cpa_dtype part_dtype, void* own_o, float* own_lse, void* o, cpa_dtype o_dtype,
     float* lse, void* workspace, size_t workspace_bytes, void* stream) {
   const char* fn = "cpa_partial_attn_paged_merged";
-  if (max_q > 1) return fail(CPA_ERR_UNSUPPORTED, "%s: decode only (max_q <= 1), got max_q = %d", fn, max_q);
   if (n_parts < 0 || n_parts > kMaxFoldParts)
     return fail(CPA_ERR_INVALID_ARG, "%s: n_parts %d not in [0, %d]", fn, n_parts, kMaxFoldParts);
   if (n_parts > 0 && (!o_parts || !lse_parts)) return fail(CPA_ERR_INVALID_ARG, "%s: part arrays are NULL", fn);
@@ -388,7 +387,7 @@ extern "C" cpa_status cpa_partial_attn_paged_merged(
                                 block_size, cp_size, cp_rank, interleave, num_seqs, max_q, hq, hkv, d, in_dtype,
                                 scale, mask, o, o_dtype, lse, workspace, workspace_bytes, &a, &empty);
   if (st != CPA_OK || empty) return st;
-  DecodeFold f{};
+  RankFold f{};
   f.n = n_parts;
   for (int j = 0; j < n_parts; ++j) {
     if (!o_parts[j] || !lse_parts[j]) return fail(CPA_ERR_INVALID_ARG, "%s: part %d pointer is NULL", fn, j);
@@ -398,5 +397,8 @@ extern "C" cpa_status cpa_partial_attn_paged_merged(
   f.part_bf16 = part_dtype == CPA_BF16;
   f.own_o = own_o;
   f.own_lse = own_lse;
-  return launch_attn_decode(a, (hipStream_t)stream, &f);
+  if (max_q == 1) return launch_attn_decode(a, (hipStream_t)stream, &f);
+  if (!attn_pp_supported(a))
+    return fail(CPA_ERR_UNSUPPORTED, "%s: prefill (max_q > 1) needs an even GQA group (hq / hkv)", fn);
+  return launch_attn_pp(&a, 1, /*paged=*/true, (hipStream_t)stream, nullptr, 0, nullptr, nullptr, &f);
 }

@@ -363,7 +363,7 @@ void launch_split_d(const DecParams& p, hipStream_t st) {
 }
 
 template <int D>
-void launch_merge_d(const DecParams& p, bool o_bf16, const DecodeFold* fold, hipStream_t st) {
+void launch_merge_d(const DecParams& p, bool o_bf16, const RankFold* fold, hipStream_t st) {
   const dim3 grid((uint32_t)cdiv((int64_t)p.num_seqs * p.hq, kWaves)), block(kThreads);
   if (!fold) {
     if (o_bf16) hipLaunchKernelGGL((decode_merge_kernel<D, true, false, false>), grid, block, 0, st, p);
@@ -384,7 +384,7 @@ size_t decode_workspace_bytes(int32_t num_seqs, int32_t max_blocks, int32_t bloc
   return (size_t)num_seqs * hq * n_splits * (d + 1) * sizeof(float);
 }
 
-cpa_status launch_attn_decode(const AttnArgs& a, hipStream_t st, const DecodeFold* fold) {
+cpa_status launch_attn_decode(const AttnArgs& a, hipStream_t st, const RankFold* fold) {
   DecParams p{};
   p.q = (const uint16_t*)a.q;
   p.q_pos = a.q_pos;

@@ -568,6 +568,85 @@ __global__ __launch_bounds__(kThreads, 1) void attn_pp_kernel(PPParams p) {
       return;
     }
   }
+  if constexpr (PAGED) {
+    if (p.n_fold > 0 || p.own_o || p.own_lse) {
+      // this rank's partial merged with the other ranks' partials of the row,
+      // by the rule of the LSE merge in base 2: weights 2^(lse_s - lse) with
+      // lse = M + log2(sum_s 2^(lse_s - M)); a part with LSE -inf has weight 0
+      // and its O is not read
+      const int64_t li = (int64_t)my_row * p.hq + h;
+      const float lse_own = l_tot > 0.f ? m_run + hw_log2(l_tot) : kNegInf;
+      if (p.own_o) {
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db) {
+#pragma unroll
+          for (int q4 = 0; q4 < 4; ++q4) {
+            const int d0 = 32 * db + 8 * q4 + 4 * lc;
+            const f32x4 val = {oacc[db][4 * q4] * inv, oacc[db][4 * q4 + 1] * inv, oacc[db][4 * q4 + 2] * inv,
+                               oacc[db][4 * q4 + 3] * inv};
+            if (p.fold_bf16) {
+              const u32x2 w = {pack_bf16x2(val[0], val[1]), pack_bf16x2(val[2], val[3])};
+              *(u32x2*)((uint16_t*)p.own_o + obase + d0) = w;
+            } else {
+              *(f32x4*)((float*)p.own_o + obase + d0) = val;
+            }
+          }
+        }
+      }
+      if (p.own_lse && lc == 0) p.own_lse[li] = lse_own * kLn2;
+      float mx = lse_own;
+      for (int j = 0; j < p.n_fold; ++j) mx = fmaxf(mx, p.fold_lse[j][li] * kLog2e);
+      float lt = kNegInf;
+      if (mx == kNegInf) {
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db) oacc[db] = f32x16{};
+      } else {
+        float sum = hw_exp2(lse_own - mx);
+        for (int j = 0; j < p.n_fold; ++j) sum += hw_exp2(p.fold_lse[j][li] * kLog2e - mx);
+        lt = mx + hw_log2(sum);
+        const float w_own = hw_exp2(lse_own - lt) * inv;  // oacc is not yet normalised
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db) oacc[db] *= w_own;
+        for (int j = 0; j < p.n_fold; ++j) {
+          const float w = hw_exp2(p.fold_lse[j][li] * kLog2e - lt);
+          if (w != 0.f) {
+#pragma unroll
+            for (int db = 0; db < D / 32; ++db) {
+#pragma unroll
+              for (int q4 = 0; q4 < 4; ++q4) {
+                const int d0 = 32 * db + 8 * q4 + 4 * lc;
+                f32x4 x;
+                if (p.fold_bf16) {
+                  const u32x2 r = *(const u32x2*)((const uint16_t*)p.fold_o[j] + obase + d0);
+                  x = f32x4{bf16_lo(r[0]), bf16_hi(r[0]), bf16_lo(r[1]), bf16_hi(r[1])};
+                } else {
+                  x = *(const f32x4*)((const float*)p.fold_o[j] + obase + d0);
+                }
+#pragma unroll
+                for (int e = 0; e < 4; ++e) oacc[db][4 * q4 + e] = fmaf(w, x[e], oacc[db][4 * q4 + e]);
+              }
+            }
+          }
+        }
+      }
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db) {
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const int d0 = 32 * db + 8 * q4 + 4 * lc;
+          const f32x4 val = {oacc[db][4 * q4], oacc[db][4 * q4 + 1], oacc[db][4 * q4 + 2], oacc[db][4 * q4 + 3]};
+          if constexpr (OUT_BF16) {
+            const u32x2 w = {pack_bf16x2(val[0], val[1]), pack_bf16x2(val[2], val[3])};
+            *(u32x2*)((uint16_t*)p.o[0] + obase + d0) = w;
+          } else {
+            *(f32x4*)((float*)p.o[0] + obase + d0) = val;
+          }
+        }
+      }
+      if (lc == 0) p.lse[0][li] = lt * kLn2;
+      return;
+    }
+  }
 #pragma unroll
   for (int db = 0; db < D / 32; ++db) {
 #pragma unroll
@@ -726,8 +805,10 @@ size_t attn_pp_order_bytes(int n_shards, int num_seqs, int max_q) {
 }
 
 cpa_status launch_attn_pp(const AttnArgs* shards, int n_shards, bool paged, hipStream_t st, void* order_ws,
-                          size_t order_ws_bytes, const MergedOut* merged, const AccumIO* accum) {
+                          size_t order_ws_bytes, const MergedOut* merged, const AccumIO* accum, const RankFold* fold) {
   if (merged && paged) return fail(CPA_ERR_INVALID_ARG, "partial attention: a merged walk needs contiguous shards");
+  if (fold && (!paged || n_shards != 1 || fold->n < 0 || fold->n > kMaxFoldParts))
+    return fail(CPA_ERR_INVALID_ARG, "partial attention: folding other ranks' partials needs one paged shard");
   if (accum && (paged || merged || n_shards != 1))
     return fail(CPA_ERR_INVALID_ARG, "partial attention: a running merge takes one contiguous shard");
   if (n_shards < 1 || n_shards > kMaxShards) return fail(CPA_ERR_INVALID_ARG, "partial attention: bad shard count");
@@ -754,6 +835,16 @@ cpa_status launch_attn_pp(const AttnArgs* shards, int n_shards, bool paged, hipS
     p.lse_acc = accum->lse_acc;
     p.o[0] = accum->o_out;
     p.lse[0] = nullptr;
+  }
+  if (fold) {
+    p.n_fold = fold->n;
+    p.fold_bf16 = fold->part_bf16;
+    for (int j = 0; j < fold->n; ++j) {
+      p.fold_o[j] = fold->o[j];
+      p.fold_lse[j] = fold->lse[j];
+    }
+    p.own_o = fold->own_o;
+    p.own_lse = fold->own_lse;
   }
   p.block_table = a.block_table;
   p.max_blocks = a.max_blocks;

@@ -77,6 +77,16 @@ struct PPParams {
   // copy of the merged O in the output dtype.
   float* o_acc;
   float* lse_acc;
+  // Paged (one shard): the other ranks' partials of the same rows, merged into
+  // this partial in the epilogue when n_fold > 0 or own_o / own_lse is set
+  // (o[0], lse[0] then receive the merge, own_o / own_lse this rank's own
+  // partial in the parts' dtype).
+  int n_fold;
+  bool fold_bf16;
+  const void* fold_o[kMaxFoldParts];
+  const float* fold_lse[kMaxFoldParts];
+  void* own_o;
+  float* own_lse;
 };
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));

@@ -59,6 +59,20 @@ struct AttnArgs {
   size_t workspace_bytes = 0;
 };
 
+// Other ranks' partials (O, LSE) of the same rows, folded into this rank's
+// own partial by the kernel that finishes it (the decode merge kernel, or the
+// paged prefill kernel's epilogue): a.o, a.lse receive the exact merge of this
+// rank's partial with o[0..n), and own_o / own_lse (either may be NULL)
+// receive this rank's own partial in the parts' dtype.
+constexpr int kMaxFoldParts = 15;
+struct RankFold {
+  int n;
+  const void* o[kMaxFoldParts];
+  const float* lse[kMaxFoldParts];
+  bool part_bf16;
+  void* own_o;
+  float* own_lse;
+};
 cpa_status launch_attn_f32(const AttnArgs& a, hipStream_t st);
 cpa_status launch_attn_mfma(const AttnArgs& a, bool paged, hipStream_t st);
 // Two-group workgroup for GQA groups of even size (hq / hkv even); one launch
@@ -92,23 +106,12 @@ struct AccumIO {
   float* lse_acc;
   void* o_out;
 };
+// With `fold` (paged, one shard), the epilogue merges the other ranks'
+// partials of its rows into the rank's own partial (see RankFold).
 cpa_status launch_attn_pp(const AttnArgs* shards, int n_shards, bool paged, hipStream_t st,
                           void* order_ws = nullptr, size_t order_ws_bytes = 0, const MergedOut* merged = nullptr,
-                          const AccumIO* accum = nullptr);
+                          const AccumIO* accum = nullptr, const RankFold* fold = nullptr);
 size_t decode_workspace_bytes(int32_t num_seqs, int32_t max_blocks, int32_t block_size, int32_t hq, int32_t d);
-// With `fold`, the decode merge also folds other ranks' partials (O, LSE) of
-// the same rows into the result: a.o, a.lse receive the exact merge of this
-// rank's partial with fold->o[0..n), and fold->own_o / own_lse (either may be
-// NULL) receive this rank's own partial in the parts' dtype.
-constexpr int kMaxFoldParts = 15;
-struct DecodeFold {
-  int n;
-  const void* o[kMaxFoldParts];
-  const float* lse[kMaxFoldParts];
-  bool part_bf16;
-  void* own_o;
-  float* own_lse;
-};
-cpa_status launch_attn_decode(const AttnArgs& a, hipStream_t st, const DecodeFold* fold = nullptr);
+cpa_status launch_attn_decode(const AttnArgs& a, hipStream_t st, const RankFold* fold = nullptr);
 
 }  // namespace cpa

@@ -7,10 +7,12 @@ movement, and runs the hot path of each schedule:
   pass_kv  one partial per KV shard (the rank's own shard first, then ranks
            r-1, r-2, ... mod cp), then the cp-way merge
   pass_q   one partial of all new queries per rank's paged round-robin shard
-           (every rank's pool resident in this GPU's memory), then the merge
+           (every rank's pool resident in this GPU's memory)
   decode   one partial per rank's paged round-robin shard for the single query
-           of every sequence; the rank's own partial is merged with the other
-           ranks' (resident) partials inside its own decode launches
+           of every sequence
+  (paged)  the rank's own partial is merged with the other ranks' (resident)
+           partials inside its own launches (pass-Q: the prefill kernel's
+           epilogue; decode: the decode merge kernel)
 
 The CPU oracle never sees anything built here except the raw draws of
 workloads.draw_sequence, which both sides share.
@@ -238,11 +240,12 @@ class Runner:
             fn()
         return graph
 
-    def decode_fold(self, stream=None, own=True):
-        """Decode: the rank's own partial against its paged shard, merged in
-        the same call with the other ranks' partials already in o_parts /
-        lse_parts (self.o, self.lse receive the result). With `own`, the rank's
-        own partial is also written to its o_parts / lse_parts entry."""
+    def rank_fold(self, stream=None, own=True):
+        """Paged schedules (decode, pass-Q): the rank's own partial against its
+        paged shard, merged in the same call with the other ranks' partials
+        already in o_parts / lse_parts (self.o, self.lse receive the result).
+        With `own`, the rank's own partial is also written to its o_parts /
+        lse_parts entry."""
         inp, w = self.inp, self.w
         r = w.rank
         others = [i for i in range(w.cp) if i != r]
@@ -260,18 +263,26 @@ class Runner:
 
     def step(self, stream=None):
         """The rank's whole share: every partial, then the merge. Pass-KV steps
-        run as one batched launch (their shards are all resident); a decode
-        step computes the other ranks' partials (as they would arrive), then
-        the rank's own partial with the merge folded in."""
+        run as one batched launch (their shards are all resident), followed by
+        the merge; the paged schedules (decode, pass-Q) compute the other
+        ranks' partials (as they would arrive), then the rank's own partial
+        with the merge folded in."""
         if self.w.kind == "pass_kv":
             self.partials_batched(stream)
-        elif self.w.kind == "decode":
-            for i in range(self.w.cp):
-                if i != self.w.rank:
-                    self.partial(i, stream)
-            self.decode_fold(stream)
+            self.merge(stream)
             return
-        else:
+        if not self.fold_supported():  # odd GQA group in prefill: no fold
             for i in range(self.w.cp):
                 self.partial(i, stream)
-        self.merge(stream)
+            self.merge(stream)
+            return
+        for i in range(self.w.cp):
+            if i != self.w.rank:
+                self.partial(i, stream)
+        self.rank_fold(stream)
+
+    def fold_supported(self) -> bool:
+        """Whether the rank's own paged launch can fold the other ranks'
+        partials in (decode always; prefill with an even GQA group)."""
+        w = self.w
+        return w.kind == "decode" or (w.kind == "pass_q" and (w.hq // w.hkv) % 2 == 0)

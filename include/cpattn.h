@@ -375,19 +375,21 @@ cpa_status cpa_partial_attn_paged(const void* q, const int32_t* q_pos, const int
                                   size_t workspace_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------
- * cpa_partial_attn_paged_merged — decode partial attention against this
- * rank's paged shard, merged in the same call with the other ranks' partials
- * of the same rows (device).
+ * cpa_partial_attn_paged_merged — partial attention against this rank's
+ * paged shard, merged in the same call with the other ranks' partials of the
+ * same rows (device).
  *
  * [PASSKV], Purpose: in allgather decode every rank attends the gathered
- * decode queries to its round-robin share of the KV cache and the per-rank
- * partials are merged exactly. Once the other ranks' partials are resident
- * (received), this call computes the rank's own partial exactly as
- * cpa_partial_attn_paged does for max_q == 1 and folds the received ones into
- * it by the rule of cpa_lse_merge inside the decode kernels' final merge, so
- * no separate merge launch follows.
+ * decode queries to its round-robin share of the KV cache, and in pass-Q
+ * chunked prefill the new queries visit every rank's resident cache; the
+ * per-rank partials are merged exactly. Once the other ranks' partials are
+ * resident (received), this call computes the rank's own partial as
+ * cpa_partial_attn_paged does and folds the received ones into it by the rule
+ * of cpa_lse_merge in the kernel that finishes it (the decode kernels' final
+ * merge; the prefill kernel's epilogue), so no separate merge launch follows.
  *
- * In: every argument of cpa_partial_attn_paged, with max_q <= 1 (decode);
+ * In: every argument of cpa_partial_attn_paged (max_q > 1 needs an even GQA
+ *   group, hq / hkv);
  *   n_parts in [0, 15]; o_parts and lse_parts are HOST arrays of n_parts
  *   DEVICE pointers: o_parts[j] [Tq][hq][d] in part_dtype (CPA_F32 or
  *   CPA_BF16), lse_parts[j] [Tq][hq] natural-log LSE, -inf for a row with no
@@ -399,9 +401,9 @@ cpa_status cpa_partial_attn_paged(const void* q, const int32_t* q_pos, const int
  *   still need it. Rows of sequences without a query are not written.
  *   Outputs must not overlap the parts.
  * workspace: as cpa_partial_attn_paged (cpa_partial_attn_paged_workspace).
- * Errors: as cpa_partial_attn_paged; CPA_ERR_UNSUPPORTED for max_q > 1;
- *   CPA_ERR_INVALID_ARG for n_parts out of range, NULL part arrays or
- *   pointers, or a bad part_dtype.
+ * Errors: as cpa_partial_attn_paged; CPA_ERR_UNSUPPORTED for max_q > 1 with
+ *   an odd GQA group; CPA_ERR_INVALID_ARG for n_parts out of range, NULL part
+ *   arrays or pointers, or a bad part_dtype.
  * ------------------------------------------------------------------------- */
 cpa_status cpa_partial_attn_paged_merged(const void* q, const int32_t* q_pos, const int32_t* cu_q,
                                          const void* k_cache, const void* v_cache,

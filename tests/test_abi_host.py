@@ -202,7 +202,6 @@ def test_paged_merged_call_validation_before_gpu(cpa):
                                                  8, 2, 128, 0, 0.1, 1, n, parts, parts, pdt, None, None, fake, 0,
                                                  fake, ws, wsb, None)
 
-    assert call(maxq=4) == -2  # decode only
     assert call(n=16) == -1 and call(n=-1) == -1  # part count out of range
     assert call(parts=None) == -1  # NULL part arrays
     assert call(pdt=5) == -1  # bad part dtype

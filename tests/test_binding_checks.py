@@ -105,7 +105,6 @@ def test_paged_merged_checks_the_received_parts():
     head = (q, q_pos, cu_q, kc, kc.clone(), table, lens, 2, 0, 8)
     f = cpa.partial_attn_paged_merged
     _raises("must be a GPU tensor", f, *head, 1, 0.125, [o1], [l1])
-    _raises("decode", f, *head, 3, 0.125, [o1], [l1])
     _raises("same number", f, *head, 1, 0.125, [o1, o1], [l1])
     _raises(r"o_parts\[1\] has dtype", f, *head, 1, 0.125, [o1, o1.bfloat16()], [l1, l1])
     _raises(r"lse_parts\[0\] has shape", f, *head, 1, 0.125, [o1], [l1[:1]])

@@ -127,17 +127,23 @@ FOLD_CASES = [
                                    rank=0, interleave=8)),
     ("decode_fold_cp4_d64_g8", dict(kind="decode", batch=9, len_range=(1, 700), lengths=(), cp=4, rank=2,
                                     interleave=3, d=64, hq=16, hkv=2)),
+    # pass-Q: a 3-token cache, so the first new queries see keys on rank 0 only
+    ("passq_fold_cp4_short", dict(kind="pass_q", batch=2, cached=3, new=140, cp=4, rank=0, interleave=8)),
+    ("passq_fold_cp3_il5_d64", dict(kind="pass_q", batch=3, cached=513, new=130, cp=3, rank=1, interleave=5, d=64,
+                                    hq=8, hkv=1)),
 ]
 
 
 @pytest.mark.parametrize("name,changes", FOLD_CASES, ids=[c[0] for c in FOLD_CASES])
-def test_decode_fold_all_elements(cpa, wl, harness, name, changes):
-    """Decode with the other ranks' partials folded into the rank's own decode
-    launches: every element against the oracle's merge of all ranks, within
-    1e-5 of the separate merge of the same partials, the rank's own partial
-    bit-identical to the plain decode call, received rows with LSE -inf never
-    read (their O is NaN), bf16 parts, and no parts at all."""
-    w = wl.scaled(wl.WORKLOADS["allgather_decode_cp2"], name=name, seed=300 + len(name), **changes)
+def test_rank_fold_all_elements(cpa, wl, harness, name, changes):
+    """The other ranks' partials folded into the rank's own paged launches
+    (decode: its merge kernel; pass-Q: the prefill epilogue): every element
+    against the oracle's merge of all ranks, within 1e-5 of the separate merge
+    of the same partials, the rank's own partial bit-identical to the plain
+    call, received rows with LSE -inf never read (their O is NaN), bf16 parts,
+    no parts at all, and the most parts the call takes."""
+    base = "allgather_decode_cp2" if changes["kind"] == "decode" else "chunked_prefill_passq_cp4"
+    w = wl.scaled(wl.WORKLOADS[base], name=name, seed=300 + len(name), **changes)
     _say(f"case {name}")
     nan = float("nan")
     inp = harness.build(w, device="cuda", pool_fill=nan)
@@ -161,7 +167,7 @@ def test_decode_fold_all_elements(cpa, wl, harness, name, changes):
         assert n_empty > 0
     for t in (run.o, run.lse, run.o_parts[r], run.lse_parts[r]):
         t.fill_(nan)
-    run.decode_fold()
+    run.rank_fold()
     torch.cuda.synchronize()
     assert torch.equal(run.o_parts[r], own_o) and torch.equal(run.lse_parts[r], own_l)
     e = assert_close(f64(run.o), f64(run.lse), merged[0], merged[1], f"{name} folded")
@@ -203,6 +209,18 @@ def test_decode_fold_all_elements(cpa, wl, harness, name, changes):
     ref_o, ref_l = oracle.lse_merge([f64(own_o)] + [np.nan_to_num(f64(t), nan=0.0) for t in po],
                                     [f64(own_l)] + [f64(t) for t in pl])
     assert_close(f64(om), f64(lm), ref_o, ref_l, f"{name} 15 parts")
+
+
+def test_rank_fold_odd_group_prefill_unsupported(cpa, wl, harness):
+    """Pass-Q prefill with an odd GQA group runs on the one-head kernel, which
+    has no fold: refused (compute the partial and merge instead)."""
+    w = wl.scaled(wl.WORKLOADS["chunked_prefill_passq_cp4"], name="fold_g3", batch=1, cached=100, new=40, cp=2,
+                  rank=0, interleave=4, hq=6, hkv=2)
+    inp = harness.build(w, device="cuda")
+    run = harness.Runner(inp)
+    with pytest.raises(cpa.CpaError) as err:
+        run.rank_fold()
+    assert err.value.status == -2
 
 
 def test_small_bf16_output_and_no_mask(cpa, wl, harness):
