@@ -38,6 +38,7 @@ HEADLINE = "llama3_8b_128k_cp4_rank1"
 DEFAULT_WORKLOADS = [HEADLINE, "qwen2.5_3b_cp2_rank0", "chunked_prefill_passq_cp4", "allgather_decode_cp2"]
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0  # MI355X HBM3E
+XGMI_LINK_BYTES_PER_S = 153e9  # one MI355X xGMI link
 # dominant kernel of the headline step and the committed counter summary of it
 ATTN_KERNEL_SOURCES = ("attn_pp.hip", "attn_pp_common.h", "device_common.h")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_llama3_8b_128k_traffic.md")
@@ -83,6 +84,7 @@ def merge_bytes(w, rows: int, n_parts: int, out_bytes: int) -> int:
 def bench_workload(name: str, steps: int, warmup: int, next_rows: bool = True) -> dict:
     import torch
 
+    import context_partial_attention_amd as cpa
     from context_partial_attention_amd import harness
     from context_partial_attention_amd.workloads import WORKLOADS
 
@@ -234,6 +236,17 @@ def bench_workload(name: str, steps: int, warmup: int, next_rows: bool = True) -
         res["pct_bf16_peak"] = 100 * res["TFLOPs"] / PEAK_BF16_TFLOPS
         res["partial_TFLOPs"] = sum(flops) / (sum(part_ms) * 1e-3) / 1e12
         res["partial_pct_bf16_peak"] = 100 * res["partial_TFLOPs"] / PEAK_BF16_TFLOPS
+        # the pass choice's rate model with this run's partial-attention rate
+        # and one xGMI link per exchanged shard: which shard to pass, and
+        # whether its transfer hides under the step's compute
+        if w.kind == "pass_kv":
+            q_lens, kv_lens = list(inp["lens"]), list(inp["lens"])
+        else:
+            q_lens, kv_lens = [w.new] * len(inp["lens"]), list(inp["lens"])
+        res["pass_choice"] = dict(cpa.pass_cost(q_lens, kv_lens, w.hq, w.hkv, w.d, 2, w.cp, XGMI_LINK_BYTES_PER_S,
+                                                res["partial_TFLOPs"] * 1e12),
+                                  link_bytes_per_s=XGMI_LINK_BYTES_PER_S,
+                                  mfma_flops_per_s=res["partial_TFLOPs"] * 1e12)
     else:
         # decode step (the rank's split and merge launches): K and V of every
         # visible local token, q, the cp-1 received partials (fp32 O + LSE)
