@@ -531,10 +531,18 @@ __global__ __launch_bounds__(kThreads, 1) void attn_pp_kernel(PPParams p) {
     if (p.o_acc) {
       // exact merge of (o_acc, lse_acc) with this partial, in base 2: weights
       // 2^(lse_s - lse) with lse = M + log2(sum_s 2^(lse_s - M)); an empty side
-      // (LSE -inf) has weight 0 and its O is not read into the sum
+      // (LSE -inf) has weight 0 and its O does not enter the sum
       const int64_t li = (int64_t)my_row * p.hq + h;
       const float lse_new = l_tot > 0.f ? m_run + hw_log2(l_tot) : kNegInf;
       const float lse_old = p.lse_acc[li] * kLog2e;
+      // the old O is loaded together with its LSE rather than after it: a row
+      // whose LSE is -inf has its loaded values replaced by zero bits (an
+      // integer select, which no floating-point simplification can drop)
+      u32x4 old_bits[D / 32][4];
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) old_bits[db][q4] = *(const u32x4*)(p.o_acc + obase + 32 * db + 8 * q4 + 4 * lc);
       const float mx = fmaxf(lse_old, lse_new);
       float w_old = 0.f, c_new = 0.f, lse_m = kNegInf;
       if (mx != kNegInf) {
@@ -545,17 +553,19 @@ __global__ __launch_bounds__(kThreads, 1) void attn_pp_kernel(PPParams p) {
         c_new = (e_new / sum) * inv;
       }
       const bool use_old = lse_old != kNegInf;
+      // an empty partial leaves a non-empty accumulator as it is (weight 1 on
+      // the old side, exactly): only the copy in o_out is written then
+      const bool write_acc = lse_new != kNegInf || !use_old;
 #pragma unroll
       for (int db = 0; db < D / 32; ++db) {
 #pragma unroll
         for (int q4 = 0; q4 < 4; ++q4) {
           const int d0 = 32 * db + 8 * q4 + 4 * lc;
-          float* acc_p = p.o_acc + obase + d0;
-          const f32x4 old = use_old ? *(const f32x4*)acc_p : f32x4{};
+          const u32x4 ob = use_old ? old_bits[db][q4] : u32x4{0u, 0u, 0u, 0u};
           f32x4 val;
 #pragma unroll
-          for (int e = 0; e < 4; ++e) val[e] = fmaf(w_old, old[e], c_new * oacc[db][4 * q4 + e]);
-          *(f32x4*)acc_p = val;
+          for (int e = 0; e < 4; ++e) val[e] = fmaf(w_old, __uint_as_float(ob[e]), c_new * oacc[db][4 * q4 + e]);
+          if (write_acc) *(f32x4*)(p.o_acc + obase + d0) = val;
           if (p.o[0]) {
             if constexpr (OUT_BF16) {
               const u32x2 w = {pack_bf16x2(val[0], val[1]), pack_bf16x2(val[2], val[3])};
@@ -566,7 +576,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_pp_kernel(PPParams p) {
           }
         }
       }
-      if (lc == 0) p.lse_acc[li] = lse_m * kLn2;
+      if (lc == 0 && write_acc) p.lse_acc[li] = lse_m * kLn2;
       return;
     }
   }

@@ -311,9 +311,11 @@ cpa_status cpa_partial_attn_merged(int32_t n_shards, const void* q, const int32_
  *
  * In: q ... mask as cpa_partial_attn (one shard). o_acc [Tq][hq][d] float and
  *   lse_acc [Tq][hq] float (device, read and written): the merge of the
- *   earlier steps; a row with lse_acc = -inf counts as empty and its o_acc is
- *   not read (start a ring with lse_acc = -inf, or with a cpa_partial_attn
- *   result in fp32). o_out (device, may be NULL) also receives the merged O
+ *   earlier steps; a row with lse_acc = -inf counts as empty and its o_acc
+ *   values do not enter the result, whatever they are (start a ring with
+ *   lse_acc = -inf, or with a cpa_partial_attn result in fp32). A row this
+ *   step adds nothing to (no visible key) keeps its o_acc and lse_acc
+ *   untouched. o_out (device, may be NULL) also receives the merged O
  *   in o_out_dtype (for the last step, say). workspace (device, optional):
  *   cpa_partial_attn_multi_workspace(1, num_seqs, max_q) bytes for the
  *   heaviest-first launch order, as in cpa_partial_attn_multi (NULL or short:
