@@ -544,6 +544,10 @@ def main():
             "ring_accumulate_ms": h.get("ring_accumulate_ms"),
             "ring_accumulate_TFLOPs": h.get("ring_accumulate_TFLOPs"),
         },
+        # the headline step's two parts: the batched partial launch and the
+        # HBM-bound 4-way merge (warm and with caches evicted first)
+        "step_parts": {k: h.get(k) for k in ("partial_ms", "merge_ms", "merge_bytes", "merge_GBps", "merge_hbm_frac",
+                                             "merge_cold_ms", "merge_cold_GBps", "merge_cold_hbm_frac")},
     }
     line["environment"] = environment()
     if not args.no_cpu_baseline:
