@@ -419,9 +419,9 @@ def cpu_baseline(name: str, budget_s: float = 15.0, block_rows: int = 64) -> dic
 
 
 def environment() -> dict:
-    """Software versions and the device. (The clock levels the driver lists
-    in sysfs after a run are not the clock the work ran at; the roofline
-    carries the clock measured by the committed counters instead.)"""
+    """Software versions and the device. (The clock levels sysfs lists after
+    a run are not the clock the work ran at; the roofline carries the clock
+    measured by the committed counters instead.)"""
     import torch
 
     props = torch.cuda.get_device_properties(0)
