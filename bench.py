@@ -302,10 +302,15 @@ def _code_only(text: str) -> str:
 
 
 def _source_digest() -> str:
+    """Digest of the prefill kernel's code and of the flags it is compiled
+    with: counters taken on another build of it do not describe this one."""
+    from context_partial_attention_amd import build as _build
+
     h = hashlib.sha256()
     for f in ATTN_KERNEL_SOURCES:
         with open(os.path.join(ROOT, "context_partial_attention_amd", "csrc", f)) as fh:
             h.update(_code_only(fh.read()).encode())
+    h.update(" ".join(_build.HIP_FLAGS + _build.FILE_FLAGS.get(ATTN_KERNEL_SOURCES[0], [])).encode())
     return h.hexdigest()[:16]
 
 

@@ -39,6 +39,11 @@ COMMON_FLAGS = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-I", INCLUDE, "-I", CSRC
 HIP_FLAGS = [f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
              # no kernel relies on NaN semantics (masking uses -inf), so max/min need no NaN quieting
              "-fno-honor-nans"]
+# Per-source additions. The prefill kernel is built with the scheduler's
+# instruction-level-parallelism strategy: its matrix phase is ordered by hand
+# (scheduling barriers), and around it this strategy measured about 1% faster
+# on the 128K and Qwen2.5-3B-shaped launches than the default (pass-Q even).
+FILE_FLAGS = {"attn_pp.hip": ["-mllvm", "-amdgpu-sched-strategy=max-ilp"]}
 
 
 def hipcc() -> str:
@@ -52,7 +57,7 @@ def _compile(src: str, verbose: bool) -> str:
     obj = os.path.join(BUILD_DIR, os.path.basename(src) + ".o")
     cmd = [hipcc(), *COMMON_FLAGS]
     if src.endswith(".hip"):
-        cmd += HIP_FLAGS
+        cmd += HIP_FLAGS + FILE_FLAGS.get(src, [])
     cmd += ["-c", os.path.join(CSRC, src), "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
