@@ -618,3 +618,27 @@ def test_full_size_workload(cpa, wl, harness, name):
         _say(f"  part {s}: max|dO|={e[0]:.2e} max|dLSE|={e[1]:.2e} over {len(rows_)} rows")
     e = assert_close(f64(run.o[ridx]), f64(run.lse[ridx]), merged[0], merged[1], f"{name} merged")
     _say(f"  merged: max|dO|={e[0]:.2e} max|dLSE|={e[1]:.2e} over {len(rows_)} of {len(pos)} rows")
+
+
+def test_launch_past_the_sort_capacity(cpa, wl, harness):
+    """More (query tile, sequence, shard) units than the launch-order pre-pass
+    sorts (8192: here 4100 short sequences x 2 shards): the workspace query
+    reports 0 bytes and the batched launch runs in index order, searching each
+    unit's key range itself. Every element of both partials and of the merge
+    against the oracle, into NaN-filled outputs."""
+    w = wl.scaled(wl.WORKLOADS["qwen2.5_3b_cp2_rank0"], name="many_short", batch=4100, len_range=(3, 40),
+                  lengths=(), seed=77)
+    _say("case many_short (8200 tile units)")
+    inp = harness.build(w, device="cuda")
+    units = -(-inp["max_q"] // 128) * len(inp["lens"]) * w.cp
+    assert units > 8192
+    assert cpa.partial_attn_multi_workspace(w.cp, len(inp["lens"]), inp["max_q"]) == 0
+    run = harness.Runner(inp)
+    assert run.workspace is None
+    run.poison()
+    run.step()
+    torch.cuda.synchronize()
+    _, parts, merged = expected_pass_kv(inp, None)
+    for s, (o_ref, l_ref) in enumerate(parts):
+        assert_close(f64(run.o_parts[s]), f64(run.lse_parts[s]), o_ref, l_ref, f"many_short partial {s}")
+    assert_close(f64(run.o), f64(run.lse), merged[0], merged[1], "many_short merged")
