@@ -135,10 +135,6 @@ __global__ __launch_bounds__(kThreads, 1) void attn_pp_kernel(PPParams p) {
     }
   };
   int seg0_ka = 0, seg0_end = 0, n = 0;  // n: tiles of the walk
-  // paged: the block-table entries the workgroup's visible keys use, staged
-  // in LDS once, so a tile's loads do not wait on a global table read
-  __shared__ int tab_sh[PAGED ? kTabCap : 1];
-  bool tab_in_lds = false;
   if constexpr (!MERGED) {
     if (!PAGED && pre_n >= 0) {
       // the pre-pass counted the key tiles whose first key some row sees; the
@@ -150,15 +146,6 @@ __global__ __launch_bounds__(kThreads, 1) void attn_pp_kernel(PPParams p) {
     } else {
       seg_range(shard, seg0_ka, seg0_end);
       n = seg0_end > seg0_ka ? (seg0_end - seg0_ka + kBN - 1) / kBN : 0;
-    }
-    if constexpr (PAGED) {
-      const int nb = (seg0_end + 15) >> 4;  // <= max_blocks (seg0_end is clamped to it)
-      tab_in_lds = nb <= kTabCap;
-      if (tab_in_lds) {
-        const int* src = p.block_table + (int64_t)seq * p.max_blocks;
-        for (int b = tid; b < nb; b += kThreads) tab_sh[b] = src[b];
-        __syncthreads();
-      }
     }
   } else {
     for (int sg = 0; sg < p.n_shards; ++sg) {
@@ -231,37 +218,44 @@ __global__ __launch_bounds__(kThreads, 1) void attn_pp_kernel(PPParams p) {
   auto ld_piece = [&](int i) { return (lane % T::kChunksPerRow) ^ T::swz(ld_row(i)); };
   auto ld_lds = [&](uint16_t* mat, int i) { return mat + (wave * T::kLoads + i) * 512; };  // wave-uniform
   const int64_t row_stride = (int64_t)p.hkv * D;
-  // paged: physical blocks of this wave's rows in the next slot's K tile and
-  // V tile (uniform over the wave: the rows of one load instruction never
-  // leave one 16-key block, clamped or not), read one slot ahead
-  int pre_k[T::kLoads] = {};
-  int pre_v[T::kLoads] = {};
+  // paged: physical block of this wave's rows in the next slot's K tile and
+  // in its V tile, read one slot ahead. A wave loads kWaveRows consecutive
+  // rows of a tile starting at a multiple of kWaveRows, a divisor of 16, so
+  // clamped to the visible range or not its rows lie in one 16-key block:
+  // that of its clamped first row.
+  constexpr int kWaveRows = T::kLoads * T::kRowsPerLoad;
+  static_assert(16 % kWaveRows == 0, "a wave's rows of a tile must share a 16-key block");
+  int pre_k = 0, pre_v = 0;
   // direct global->LDS loads of one matrix tile; rows past the visible range
   // are clamped to its last row
-  auto load_mat = [&](const uint16_t* __restrict__ src, const TileRef& tr, const int* pre, uint16_t* mat) {
+  auto load_mat = [&](const uint16_t* __restrict__ src, const TileRef& tr, int blk, uint16_t* mat) {
     const int j0 = tr.j0, n_end = tr.end;
 #pragma unroll
     for (int i = 0; i < T::kLoads; ++i) {
       const int j = min(j0 + ld_row(i), n_end - 1);
       const uint16_t* g;
       if constexpr (PAGED) {
-        g = src + ((int64_t)pre[i] * p.hkv + kvh) * 16 * D + (j & 15) * D + ld_piece(i) * 8;
+        g = src + ((int64_t)blk * p.hkv + kvh) * 16 * D + (j & 15) * D + ld_piece(i) * 8;
       } else {
         g = src + (int64_t)j * row_stride + kvh * D + ld_piece(i) * 8;
       }
       lds_dma16(g, ld_lds(mat, i));
     }
   };
+  // The table is read with uniform indices, through the scalar cache
+  // (consecutive tiles read consecutive entries). A tile outside the walk
+  // (tile n, or tile -1 before the first V) reads an entry inside the table
+  // that no load then uses.
   auto prefetch_tab = [&](int tk, int tv) {  // K tile tk, V tile tv
     if constexpr (PAGED) {
-      const int* tab = p.block_table + (int64_t)seq * p.max_blocks;
-      auto tab_at = [&](int b) { return tab_in_lds ? tab_sh[b] : tab[b]; };
-#pragma unroll
-      for (int i = 0; i < T::kLoads; ++i) {
-        if (tk < n) pre_k[i] = __builtin_amdgcn_readfirstlane(tab_at(min(tk * kBN + ld_row(i), seg0_end - 1) >> 4));
-        if (tv >= 0 && tv < n)
-          pre_v[i] = __builtin_amdgcn_readfirstlane(tab_at(min(tv * kBN + ld_row(i), seg0_end - 1) >> 4));
-      }
+      using ctab_t = const __attribute__((address_space(4))) int*;
+      const ctab_t tab = (ctab_t)(p.block_table + (int64_t)seq * p.max_blocks);
+      const int w_row0 = wave * kWaveRows;
+      const int last = __builtin_amdgcn_readfirstlane(seg0_end - 1);
+      const int bk = __builtin_amdgcn_readfirstlane(max(0, min(tk * kBN + w_row0, last)) >> 4);
+      const int bv = __builtin_amdgcn_readfirstlane(max(0, min(tv * kBN + w_row0, last)) >> 4);
+      pre_k = tab[bk];
+      pre_v = tab[bv];
     }
   };
   // position of key tid of the tile (tid < 64): read (or derived) when the

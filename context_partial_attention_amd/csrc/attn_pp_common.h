@@ -11,7 +11,6 @@ namespace pp {
 
 constexpr int kBN = 64;        // keys per tile
 constexpr int kRows = 128;     // query rows per workgroup (per head)
-constexpr int kTabCap = 2048;  // paged: block-table entries of a workgroup staged in LDS (8 KiB)
 // launch-order entry: unit index in the low bits, its visible key-tile count
 // above them (kOrderWorkUnknown when it does not fit)
 constexpr int kOrderUnitBits = 13;

@@ -98,9 +98,8 @@ SMALL = [
     ("passq_cp4_small", dict(kind="pass_q", batch=2, cached=1000, new=300, cp=4, rank=0, interleave=8)),
     ("passq_cp3_il5_d64", dict(kind="pass_q", batch=3, cached=513, new=130, cp=3, rank=0, interleave=5, d=64,
                                hq=8, hkv=1)),
-    # a local shard of more than 2048 blocks: the prefill kernel reads the block table from HBM
-    # instead of staging it in LDS
-    ("passq_long_cache_table_in_hbm", dict(kind="pass_q", batch=1, cached=150000, new=70, cp=2, rank=1,
+    # a local shard of 75000 keys (4688 blocks): a long block table, read one entry per wave and tile
+    ("passq_long_cache", dict(kind="pass_q", batch=1, cached=150000, new=70, cp=2, rank=1,
                                            interleave=8, hq=4, hkv=2, d=64)),
     # odd GQA group: the paged prefill runs on the one-head-per-workgroup kernel
     ("passq_cp2_g3", dict(kind="pass_q", batch=2, cached=700, new=150, cp=2, rank=1, interleave=4, hq=6, hkv=2)),
