@@ -7,8 +7,8 @@
 //
 // One query per sequence makes this HBM-bound: every K/V byte of the local
 // shard is read once. The work is split over (sequence, KV head, split of
-// 512 local tokens) so that sequences of very different lengths still fill
-// the GPU, and a second small kernel merges the splits of each (sequence,
+// 512-2048 local tokens) so that sequences of very different lengths still
+// fill the GPU, and a second small kernel merges the splits of each (sequence,
 // head) with the same exact LSE rule used across ranks. That kernel can also
 // fold in the other ranks' partials of the same rows when they are already
 // resident (received), so that a rank's decode step ends with the merged
@@ -31,7 +31,17 @@
 namespace cpa {
 namespace {
 
-constexpr int kSplit = 512;  // local KV tokens per split
+// Local KV tokens per split: the largest of 2048, 1024 and 512 that still
+// gives kMinSplitItems (sequence, split) pairs at the longest local length.
+// Longer splits spend less of the run on each workgroup's first load and its
+// final reduction; shorter ones keep a few long sequences spread over the GPU.
+constexpr int kMaxSplit = 2048, kMinSplit = 512;
+constexpr int64_t kMinSplitItems = 1024;
+int split_tokens(int64_t num_seqs, int64_t max_len) {
+  int s = kMaxSplit;
+  while (s > kMinSplit && num_seqs * ((max_len + s - 1) / s) < kMinSplitItems) s >>= 1;
+  return s;
+}
 constexpr int kThreads = 256;
 constexpr int kWaves = 4;
 
@@ -45,7 +55,7 @@ struct DecParams {
   int max_blocks;
   const int* local_kv_lens;
   int cp, rank, il;
-  int num_seqs, hq, hkv, g, head_chunk, n_hchunks, n_splits_max, causal;
+  int num_seqs, hq, hkv, g, head_chunk, n_hchunks, split, n_splits_max, causal;
   float scale_log2;
   float* ws_o;    // [num_seqs][hq][n_splits_max][D]
   float* ws_lse;  // [num_seqs][hq][n_splits_max], base-2 LSE of each split
@@ -74,15 +84,17 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecParams p) {
   __shared__ float red_m[kWaves][HC], red_l[kWaves][HC];
   __shared__ __attribute__((aligned(16))) float red_o[kWaves][HC][D];
 
-  const int split = blockIdx.x;
-  const int kvh = blockIdx.y / p.n_hchunks, hc = blockIdx.y % p.n_hchunks;
+  // heads vary fastest over the grid: the workgroups that run together read
+  // the slices of the same physical blocks
+  const int split = blockIdx.y;
+  const int kvh = blockIdx.x / p.n_hchunks, hc = blockIdx.x % p.n_hchunks;
   const int seq = blockIdx.z;
   const int row = p.cu_q[seq];
   if (p.cu_q[seq + 1] <= row) return;
   const int n_vis = visible_local(p, seq, row);
-  if (split * kSplit >= n_vis) return;  // the merge kernel reads only the splits that exist
-  const int k_end = min(n_vis, (split + 1) * kSplit);
-  const int b_begin = split * (kSplit / 16), b_end = (k_end + 15) / 16;
+  if (split * p.split >= n_vis) return;  // the merge kernel reads only the splits that exist
+  const int k_end = min(n_vis, (split + 1) * p.split);
+  const int b_begin = split * (p.split / 16), b_end = (k_end + 15) / 16;
   const int h0 = kvh * p.g + hc * HC;
   const int nh = min(HC, p.g - hc * HC);
 
@@ -111,7 +123,7 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecParams p) {
   const int64_t head_stride = 16LL * D;  // one (block, kv head) slab
   // This wave's blocks are b_begin + wave + kWaves*i, i < nb (at most
   // kBlocksPerWave); lane i holds the physical block of the i-th, read once.
-  constexpr int kBlocksPerWave = kSplit / 16 / kWaves;
+  constexpr int kBlocksPerWave = kMaxSplit / 16 / kWaves;
   static_assert(kBlocksPerWave <= 64, "one block-table entry per lane");
   const int first_b = b_begin + wave;
   const int nb = first_b < b_end ? (b_end - first_b + kWaves - 1) / kWaves : 0;
@@ -272,7 +284,7 @@ __global__ __launch_bounds__(kThreads) void decode_merge_kernel(DecParams p) {
     for (int j = 0; j < kMaxFoldParts; ++j) lf[j] = j < p.n_fold ? p.fold_lse[j][ri] * kLog2e : kNegInf;
   }
   const int n_vis = visible_local(p, seq, row);
-  const int n_splits = (n_vis + kSplit - 1) / kSplit;
+  const int n_splits = (n_vis + p.split - 1) / p.split;
   const int64_t slot0 = ((int64_t)seq * p.hq + h) * p.n_splits_max;
   float mx = kNegInf;
   for (int s = lane; s < n_splits; s += 64) mx = fmaxf(mx, p.ws_lse[slot0 + s]);
@@ -348,7 +360,7 @@ int head_chunk_for(int g) { return g >= 8 ? 8 : (g >= 4 ? 4 : (g >= 2 ? 2 : 1));
 
 template <int D, int HC>
 void launch_split(const DecParams& p, hipStream_t st) {
-  const dim3 grid((uint32_t)p.n_splits_max, (uint32_t)(p.hkv * p.n_hchunks), (uint32_t)p.num_seqs);
+  const dim3 grid((uint32_t)(p.hkv * p.n_hchunks), (uint32_t)p.n_splits_max, (uint32_t)p.num_seqs);
   hipLaunchKernelGGL((decode_split_kernel<D, HC>), grid, dim3(kThreads), 0, st, p);
 }
 
@@ -380,7 +392,8 @@ void launch_merge_d(const DecParams& p, bool o_bf16, const RankFold* fold, hipSt
 }  // namespace
 
 size_t decode_workspace_bytes(int32_t num_seqs, int32_t max_blocks, int32_t block_size, int32_t hq, int32_t d) {
-  const int64_t n_splits = cdiv((int64_t)max_blocks * block_size, kSplit);
+  const int64_t max_len = (int64_t)max_blocks * block_size;
+  const int64_t n_splits = cdiv(max_len, split_tokens(num_seqs, max_len));
   return (size_t)num_seqs * hq * n_splits * (d + 1) * sizeof(float);
 }
 
@@ -403,7 +416,8 @@ cpa_status launch_attn_decode(const AttnArgs& a, hipStream_t st, const RankFold*
   p.g = a.hq / a.hkv;
   p.head_chunk = head_chunk_for(p.g);
   p.n_hchunks = (int)cdiv(p.g, p.head_chunk);
-  p.n_splits_max = (int)cdiv((int64_t)a.max_blocks * 16, kSplit);
+  p.split = split_tokens(a.num_seqs, (int64_t)a.max_blocks * 16);
+  p.n_splits_max = (int)cdiv((int64_t)a.max_blocks * 16, p.split);
   p.causal = a.causal;
   p.scale_log2 = a.scale * kLog2e;
   const int64_t slots = (int64_t)a.num_seqs * a.hq * p.n_splits_max;

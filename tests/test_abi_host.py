@@ -142,6 +142,12 @@ def test_device_call_validation_before_gpu(cpa):
     need = ctypes.c_size_t(0)
     assert lib.cpa_partial_attn_paged_workspace(2, 1, 8, 16, 8, 128, ctypes.byref(need)) == 0
     assert need.value == 2 * 8 * 1 * 129 * 4
+    # decode splits: 2048 local tokens while that leaves >= 1024 (sequence, split) pairs at the
+    # longest length, else 1024, else 512
+    for seqs, blocks, split in [(256, 1024, 2048), (128, 1024, 2048), (100, 1024, 1024), (60, 1024, 512),
+                                (16, 8192, 2048), (1, 10, 512), (512, 188, 2048), (400, 188, 1024)]:
+        assert lib.cpa_partial_attn_paged_workspace(seqs, 1, blocks, 16, 32, 128, ctypes.byref(need)) == 0
+        assert need.value == seqs * 32 * -(-blocks * 16 // split) * 129 * 4, (seqs, blocks, split)
     assert lib.cpa_partial_attn_paged_workspace(2, 7, 8, 16, 8, 128, ctypes.byref(need)) == 0 and need.value == 0
     # merge: too many parts, bad d
     ptrs = (ctypes.c_void_p * 17)(*([0x1000] * 17))

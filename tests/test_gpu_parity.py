@@ -107,6 +107,12 @@ SMALL = [
                               interleave=8)),
     ("decode_cp4_d64_g8", dict(kind="decode", batch=9, len_range=(1, 700), lengths=(), cp=4, rank=0, interleave=3,
                                d=64, hq=16, hkv=2)),
+    # enough sequences for the decode kernel's longer splits (2048 and 1024 local tokens; the split
+    # size is checked through the workspace size), several splits per sequence with ragged ends
+    ("decode_512seqs_split2048", dict(kind="decode", batch=512, len_range=(1, 6000), lengths=(), cp=2, rank=1,
+                                      interleave=8)),
+    ("decode_400seqs_split1024", dict(kind="decode", batch=400, len_range=(1, 6000), lengths=(), cp=2, rank=0,
+                                      interleave=8, hq=8, hkv=2)),
 ]
 
 
@@ -117,7 +123,13 @@ def test_small_bf16_all_elements(cpa, wl, harness, name, changes):
     w = wl.scaled(wl.WORKLOADS[base], name=name, seed=100 + len(name), **changes)
     _say(f"case {name}")
     # NaN in every unused cache slot: any read of one would show up in the results
-    _check_schedule(harness, w, pool_fill=float("nan"))
+    inp, _, _ = _check_schedule(harness, w, pool_fill=float("nan"))
+    if "_split" in name:
+        split = int(name.rsplit("split", 1)[1])
+        max_blocks = inp["ranks"][w.rank]["block_table"].shape[1]
+        need = cpa.partial_attn_paged_workspace(w.batch, 1, max_blocks, 16, w.hq, w.d)
+        n_splits = need // (w.batch * w.hq * (w.d + 1) * 4)
+        assert max_blocks * 16 > split and n_splits == -(-max_blocks * 16 // split), (max_blocks, n_splits)
 
 
 FOLD_CASES = [
