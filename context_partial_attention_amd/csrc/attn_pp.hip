@@ -216,7 +216,11 @@ __global__ __launch_bounds__(kThreads, 1) void attn_pp_kernel(PPParams p) {
   const int ld_rowbase = wave * T::kLoads * T::kRowsPerLoad + lane / T::kChunksPerRow;
   auto ld_row = [&](int i) { return ld_rowbase + i * T::kRowsPerLoad; };
   auto ld_piece = [&](int i) { return (lane % T::kChunksPerRow) ^ T::swz(ld_row(i)); };
-  auto ld_lds = [&](uint16_t* mat, int i) { return mat + (wave * T::kLoads + i) * 512; };  // wave-uniform
+  // LDS byte address of load instruction i of this wave in the matrix that
+  // starts mat_off elements into smem (wave-uniform)
+  const uint32_t wave_lds = __builtin_amdgcn_readfirstlane(
+      (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint16_t*)smem + (uint32_t)wave * T::kLoads * 1024u);
+  auto ld_lds = [&](int mat_off, int i) { return wave_lds + (uint32_t)mat_off * 2u + (uint32_t)i * 1024u; };
   const int64_t row_stride = (int64_t)p.hkv * D;
   // paged: physical block of this wave's rows in the next slot's K tile and
   // in its V tile, read one slot ahead. A wave loads kWaveRows consecutive
@@ -226,10 +230,28 @@ __global__ __launch_bounds__(kThreads, 1) void attn_pp_kernel(PPParams p) {
   constexpr int kWaveRows = T::kLoads * T::kRowsPerLoad;
   static_assert(16 % kWaveRows == 0, "a wave's rows of a tile must share a 16-key block");
   int pre_k = 0, pre_v = 0;
+  // contiguous shards: byte offset of this lane's piece of load instruction i
+  // from the start of the tile's first row, the same in every tile that needs
+  // no clamping
+  uint32_t ld_off[T::kLoads];
+#pragma unroll
+  for (int i = 0; i < T::kLoads; ++i) ld_off[i] = (uint32_t)(ld_row(i) * (int)row_stride + ld_piece(i) * 8) * 2u;
+  const int kvh_u = __builtin_amdgcn_readfirstlane(kvh);
   // direct global->LDS loads of one matrix tile; rows past the visible range
-  // are clamped to its last row
-  auto load_mat = [&](const uint16_t* __restrict__ src, const TileRef& tr, int blk, uint16_t* mat) {
+  // are clamped to its last row. In a contiguous shard a tile with every row
+  // visible (all but the last) is addressed from a uniform base, with no
+  // vector arithmetic (paged tiles measured slower that way: their base waits
+  // on the block-table read).
+  auto load_mat = [&](const uint16_t* __restrict__ src, const TileRef& tr, int blk, int mat) {
     const int j0 = tr.j0, n_end = tr.end;
+    if constexpr (!PAGED) {
+      if (__builtin_amdgcn_readfirstlane(j0 + kBN <= n_end)) {
+        const uint16_t* base = src + (int64_t)__builtin_amdgcn_readfirstlane(j0) * row_stride + kvh_u * D;
+#pragma unroll
+        for (int i = 0; i < T::kLoads; ++i) lds_dma16_s(base, ld_off[i], ld_lds(mat, i));
+        return;
+      }
+    }
 #pragma unroll
     for (int i = 0; i < T::kLoads; ++i) {
       const int j = min(j0 + ld_row(i), n_end - 1);
@@ -291,11 +313,11 @@ __global__ __launch_bounds__(kThreads, 1) void attn_pp_kernel(PPParams p) {
         kp_j0 = tr.j0;
         kp_end = tr.end;
       }
-      load_mat(tr.k, tr, pre_k, kslot(t & 1));
+      load_mat(tr.k, tr, pre_k, (t & 1) * T::kSlotElems);
     }
     if (t >= 1) {
       const TileRef vr = MERGED ? prev_tr : tile_ref(t - 1);
-      load_mat(vr.v, vr, pre_v, vslot(t & 1));
+      load_mat(vr.v, vr, pre_v, (t & 1) * T::kSlotElems + T::kKElems);
     }
     prev_tr = tr;
   };

@@ -107,9 +107,9 @@ __device__ __forceinline__ s16x4 lds_read_tr(const uint16_t* p) {
 // for these loads (vmcnt 0) itself before the barrier that publishes the
 // slot. Loads the compiler issues itself are counted in order with these, so
 // its own waits can only wait longer than needed, never shorter.
-__device__ __forceinline__ void lds_dma16(const void* src, const uint16_t* lds_base) {
-  const uint32_t m0v = __builtin_amdgcn_readfirstlane(
-      (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint16_t*)lds_base);
+// lds_addr is the LDS byte address (wave-uniform).
+__device__ __forceinline__ void lds_dma16(const void* src, uint32_t lds_addr) {
+  const uint32_t m0v = __builtin_amdgcn_readfirstlane(lds_addr);
   // m0 is reserved to the compiler (a clobber of it is ignored), so the
   // statement restores it
   uint32_t saved;
@@ -119,6 +119,17 @@ __device__ __forceinline__ void lds_dma16(const void* src, const uint16_t* lds_b
                : "memory");
 }
 
+// The same load addressed as a wave-uniform base (scalar registers) plus this
+// lane's 32-bit byte offset, so a tile whose per-lane offsets do not change
+// costs no vector arithmetic to address.
+__device__ __forceinline__ void lds_dma16_s(const void* base, uint32_t off, uint32_t lds_addr) {
+  const uint32_t m0v = __builtin_amdgcn_readfirstlane(lds_addr);
+  uint32_t saved;
+  asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %3\n\tglobal_load_lds_dwordx4 %1, %2\n\ts_mov_b32 m0, %0"
+               : "=&s"(saved)
+               : "v"(off), "s"(base), "s"(m0v)
+               : "memory");
+}
 
 // Value of the lane 32 apart (lane ^ 32), combined: v_permlane32_swap
 // exchanges the upper half of one register with the lower half of another;
