@@ -446,6 +446,97 @@ def environment() -> dict:
     return env
 
 
+def power_probe(seconds: float = 5.0):
+    """Board power and shader clock (sysfs, sampled every 0.1 s) while one
+    piece of work repeats for `seconds`: a 8192^3 bf16 matrix product
+    (torch.matmul) with N(0, 1) operands and with zero operands, then the
+    step of every workload. One JSON line per piece. The product is the
+    reference for the dense bf16 rate the chip sustains at its power limit."""
+    import glob
+    import threading
+
+    import torch
+
+    from context_partial_attention_amd import harness
+    from context_partial_attention_amd.workloads import WORKLOADS
+
+    def first(pattern):
+        f = sorted(glob.glob(pattern))
+        return f[0] if f else None
+
+    pw = first("/sys/class/drm/card*/device/hwmon/hwmon*/power1_average") or \
+        first("/sys/class/drm/card*/device/hwmon/hwmon*/power1_input")
+    sclk = first("/sys/class/drm/card*/device/pp_dpm_sclk")
+
+    def sample():
+        w = mhz = None
+        try:
+            w = int(open(pw).read()) / 1e6 if pw else None
+        except (OSError, ValueError):
+            pass
+        try:
+            for line in open(sclk) if sclk else []:
+                if "*" in line:
+                    mhz = int(line.split(":")[1].strip().lower().split("mhz")[0])
+        except (OSError, ValueError, IndexError):
+            pass
+        return w, mhz
+
+    def run(label, fn, flops=None):
+        samples, done = [], threading.Event()
+
+        def sampler():
+            while not done.is_set():
+                samples.append(sample())
+                time.sleep(0.1)
+
+        fn()
+        torch.cuda.synchronize()
+        th = threading.Thread(target=sampler)
+        n, t0 = 0, time.time()
+        th.start()
+        while time.time() < t0 + seconds:
+            fn()
+            n += 1
+            if n % 8 == 0:
+                torch.cuda.synchronize()
+        torch.cuda.synchronize()
+        el = time.time() - t0
+        done.set()
+        th.join()
+        # the first second is the ramp from idle
+        steady = samples[len(samples) // 5:]
+        ws = sorted(x[0] for x in steady if x[0] is not None)
+        cs = sorted(x[1] for x in steady if x[1] is not None)
+        out = {"work": label, "calls": n, "seconds": round(el, 2), "ms_per_call": round(el / n * 1e3, 4),
+               "power_W_median": ws[len(ws) // 2] if ws else None, "sclk_MHz_median": cs[len(cs) // 2] if cs else None}
+        if flops:
+            out["TFLOPs"] = round(flops * n / el / 1e12, 1)
+        print(json.dumps(out), flush=True)
+
+    a = torch.randn(8192, 8192, device="cuda", dtype=torch.bfloat16)
+    b = torch.randn(8192, 8192, device="cuda", dtype=torch.bfloat16)
+    c = torch.empty_like(a)
+    run("matmul bf16 8192^3, N(0,1) operands", lambda: torch.matmul(a, b, out=c), 2 * 8192 ** 3)
+    a.zero_()
+    b.zero_()
+    run("matmul bf16 8192^3, zero operands", lambda: torch.matmul(a, b, out=c), 2 * 8192 ** 3)
+    del a, b, c
+    for name in DEFAULT_WORKLOADS:
+        w = WORKLOADS[name]
+        inp = harness.build(w, device="cuda", keep_full=False)
+        r = harness.Runner(inp)
+        if w.kind == "pass_kv":
+            run(f"{name}: batched partials + merge", r.step)
+        else:  # the other ranks' partials arrive once; the rank's own launch folds them in
+            for i in range(w.cp):
+                if i != w.rank:
+                    r.partial(i)
+            run(f"{name}: the rank's own launch with the fold", r.rank_fold)
+        del r, inp
+        torch.cuda.empty_cache()
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -457,6 +548,8 @@ def main():
                     help="skip the fused-merge walk and running-merge timings (profiling the partials kernel alone)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain device-to-device copy of 256 MiB (x4) to scale HBM byte counters")
+    ap.add_argument("--power-probe", action="store_true",
+                    help="only sample board power and shader clock under a bf16 matmul and each workload's step")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for --gpus {args.gpus}); "
@@ -478,6 +571,9 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         print(json.dumps({"calibrate_copy_bytes_per_dispatch": n, "dispatches": 4}), flush=True)
+        return
+    if args.power_probe:
+        power_probe()
         return
     names = [n for n in args.workloads.split(",") if n]
     if HEADLINE not in names:
