@@ -702,20 +702,36 @@ __global__ __launch_bounds__(kThreads, 1) void attn_pp_kernel(PPParams p) {
 // every unit's key tiles (a binary search over the first positions of the
 // shard's key tiles) and counting-sorts the units by it, descending. Units
 // of equal work keep no particular order; the results do not depend on it.
-// Each entry also carries the unit's count, so the attention kernel starts
-// its first tile loads without searching the key positions itself.
+// When the launch holds several shards and is long against its heaviest
+// unit (each CU's share of the key tiles at least kShardMajorRatio times the
+// heaviest unit's), the order is shard-major instead, heaviest first within
+// each shard (counts from 511 tiles up rank as equal there): the workgroups
+// running together then read the K/V of one shard, which the L2 keeps, and
+// the heavy units of the last shard still start early enough for the end of
+// the launch to stay short. Each entry also carries the unit's count, so the
+// attention kernel starts its first tile loads without searching the key
+// positions itself.
 constexpr int kSchedThreads = 1024;
 constexpr int kSchedBuckets = 4096;
 constexpr int kSchedMaxUnits = 8192;
+constexpr int kShardMajorRatio = 12;
 
+// wg_per_unit: workgroups per unit (KV heads x head pairs); n_cus: compute
+// units of the device
 __global__ __launch_bounds__(kSchedThreads) void pp_schedule_kernel(PPParams p, int n_units, int merged,
-                                                                     int* order) {
+                                                                     int wg_per_unit, int n_cus, int* order) {
   static_assert(kSchedMaxUnits <= 1 << kOrderUnitBits, "unit index must fit its field");
   __shared__ int bucket[kSchedBuckets];
   __shared__ int work_sh[kSchedMaxUnits];
   __shared__ int wave_tot[kSchedThreads / 64];
+  __shared__ unsigned long long total_sh;
+  __shared__ int max_sh;
   const int tid = threadIdx.x;
   for (int b = tid; b < kSchedBuckets; b += kSchedThreads) bucket[b] = 0;
+  if (tid == 0) {
+    total_sh = 0;
+    max_sh = 0;
+  }
   __syncthreads();
   // a unit is (tile_desc, seq, shard), or (tile_desc, seq) when merged (its
   // work is then summed over the shards it walks)
@@ -749,8 +765,21 @@ __global__ __launch_bounds__(kSchedThreads) void pp_schedule_kernel(PPParams p, 
       }
     }
     work_sh[u] = work;
-    atomicAdd(&bucket[min(work, kSchedBuckets - 1)], 1);
+    atomicAdd(&total_sh, (unsigned long long)work);
+    atomicMax(&max_sh, work);
   }
+  __syncthreads();
+  // sort key: the work, or (shard-major) the shard's rank above the work
+  constexpr int kPerShard = kSchedBuckets / kMaxShards;
+  const bool shard_major = !merged && p.n_shards > 1 &&
+                           total_sh * (unsigned long long)wg_per_unit >=
+                               (unsigned long long)kShardMajorRatio * (unsigned long long)max_sh * n_cus;
+  auto key = [&](int u) {
+    const int work = work_sh[u];
+    if (!shard_major) return min(work, kSchedBuckets - 1);
+    return (p.n_shards - 1 - u % p.n_shards) * kPerShard + min(work, kPerShard - 1);
+  };
+  for (int u = tid; u < n_units; u += kSchedThreads) atomicAdd(&bucket[key(u)], 1);
   __syncthreads();
   // exclusive scan over the buckets in descending key order: thread t owns
   // the four buckets 4095-4t .. 4092-4t
@@ -780,7 +809,7 @@ __global__ __launch_bounds__(kSchedThreads) void pp_schedule_kernel(PPParams p, 
   __syncthreads();
   for (int u = tid; u < n_units; u += kSchedThreads) {
     const int work = work_sh[u];
-    order[atomicAdd(&bucket[min(work, kSchedBuckets - 1)], 1)] =
+    order[atomicAdd(&bucket[key(u)], 1)] =
         u | (min(work, kOrderWorkUnknown) << kOrderUnitBits);
   }
 }
@@ -896,8 +925,11 @@ cpa_status launch_attn_pp(const AttnArgs* shards, int n_shards, bool paged, hipS
   if (order_bytes > 0 && order_ws && order_ws_bytes >= order_bytes) {
     p.order = (const int*)order_ws;
     const int n_units = (int)(n_groups / a.hkv);
+    int dev = 0, n_cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&n_cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+      return fail(CPA_ERR_HIP, "partial attention: cannot read the device's compute-unit count");
     hipLaunchKernelGGL(pp_schedule_kernel, dim3(1), dim3(kSchedThreads), 0, st, p, n_units, merged ? 1 : 0,
-                       (int*)order_ws);
+                       a.hkv * (p.g / 2), n_cus, (int*)order_ws);
   }
   if (merged) {
     if (a.d == 64) merged->o_bf16 ? pp_launch<64, false, true, true>(p, nb, st) : pp_launch<64, false, false, true>(p, nb, st);

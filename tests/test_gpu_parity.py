@@ -303,10 +303,15 @@ def test_multi_shard_launch_equals_separate_calls(cpa, wl, harness, name, change
 
 
 # many short sequences: 2000 and 2200 (shard, sequence) segments, 6000 and
-# 6600 units for the ordering pre-pass
+# 6600 units for the ordering pre-pass; a few sequences of a few thousand
+# tokens, a short launch against its heaviest unit (ordered heaviest first);
+# two long sequences, a long launch (ordered shard-major)
 PREPASS = [
     ("seqs_1000_cp2_r0", dict(batch=1000, len_range=(1, 700), lengths=(), cp=2, rank=0, hq=4, hkv=2, d=64)),
     ("seqs_1100_cp2_r1", dict(batch=1100, len_range=(1, 700), lengths=(), cp=2, rank=1, hq=4, hkv=2, d=64)),
+    ("few_heaviest_first_cp2_r0", dict(batch=4, lengths=(2453, 3682, 4327, 6706), len_range=(), cp=2, rank=0)),
+    ("long_shard_major_cp2_r1", dict(batch=2, lengths=(100000, 70001), len_range=(), cp=2, rank=1, hq=16, hkv=2,
+                                     d=64)),
 ]
 
 
@@ -318,7 +323,8 @@ def test_ordering_prepass_segments(cpa, wl, harness, name, changes):
     w = wl.scaled(wl.WORKLOADS["qwen2.5_3b_cp2_rank0"], name=name, seed=700 + len(name), **changes)
     _say(f"case prepass {name}")
     inp = harness.build(w, device="cuda")
-    assert inp["max_q"] <= 3 * 128, "the units must fit the pre-pass (8192)"
+    n_units = -(-inp["max_q"] // 128) * w.batch * w.cp
+    assert n_units <= 8192, "the units must fit the pre-pass"
     run = harness.Runner(inp)
     assert run.workspace is not None
     for i in range(w.cp):
@@ -333,6 +339,27 @@ def test_ordering_prepass_segments(cpa, wl, harness, name, changes):
     for s, (o, l) in enumerate(sep):
         assert torch.equal(run.o_parts[s], o), f"{name} shard {s}: O differs from the separate call"
         assert torch.equal(run.lse_parts[s], l), f"{name} shard {s}: LSE differs from the separate call"
+    # the order itself (the workspace starts with one entry per unit: the unit index in the low 13
+    # bits, its visible key-tile count above): a permutation of the units, heaviest first (counts
+    # from 4095 tiles up rank as equal), or, when each CU's share of the launch's key tiles is at
+    # least 12 times the heaviest unit's, shard-major with the heaviest first within each shard
+    # (counts from 511 up rank as equal)
+    e = run.workspace[: 4 * n_units].view(torch.int32).cpu().numpy().astype(np.int64)
+    unit, work = e & 8191, e >> 13
+    assert np.array_equal(np.sort(unit), np.arange(n_units))
+    shard = unit % w.cp
+    n_cus = torch.cuda.get_device_properties(0).multi_processor_count
+    shard_major = int(work.sum()) * w.hkv * (w.hq // w.hkv // 2) >= 12 * int(work.max()) * n_cus
+    if name.startswith("long"):
+        assert shard_major and work.max() > 511
+    if name.startswith("few"):
+        assert not shard_major
+    if shard_major:
+        assert np.all(np.diff(shard) >= 0), "shard-major"
+        for sh in range(w.cp):
+            assert np.all(np.diff(np.minimum(work[shard == sh], 511)) <= 0), f"shard {sh}: heaviest first"
+    else:
+        assert np.all(np.diff(np.minimum(work, 4095)) <= 0), "heaviest first"
 
 
 MERGED = [
