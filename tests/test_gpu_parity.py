@@ -113,6 +113,9 @@ SMALL = [
                                       interleave=8)),
     ("decode_400seqs_split1024", dict(kind="decode", batch=400, len_range=(1, 6000), lengths=(), cp=2, rank=0,
                                       interleave=8, hq=8, hkv=2)),
+    # one 200K-token context and a short one: 196 splits of 512 local tokens for the long one
+    ("decode_long_200k_split512", dict(kind="decode", batch=2, lengths=(200000, 37), len_range=(), cp=2, rank=1,
+                                       interleave=8)),
 ]
 
 
