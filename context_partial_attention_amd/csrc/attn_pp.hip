@@ -39,9 +39,10 @@
 // online softmax, which yields the exact merge of the shards' partials. With a
 // running accumulator (o_acc) the epilogue folds the partial into it instead
 // of writing it. An optional pre-pass (pp_schedule_kernel) orders the launch
-// heaviest query tile first. Paged shards (pass-Q prefill) take one shard;
-// there the epilogue can also merge the other ranks' partials of the same
-// rows into the result (the rank fold).
+// heaviest query tile first (shard-major for long launches). Paged shards
+// (pass-Q prefill) take one shard, their block table read through the scalar
+// cache; there the epilogue can also merge the other ranks' partials of the
+// same rows into the result (the rank fold).
 #include <climits>
 #include <mutex>
 
