@@ -60,14 +60,18 @@ __global__ __launch_bounds__(kThreads, 1) void attn_pp_kernel(PPParams p) {
   __shared__ __attribute__((aligned(16))) uint16_t smem[2 * T::kSlotElems];
   __shared__ int kpos_sh[4][kBN];
 
-  // ---- (sequence, query tile, KV head) group and head pair; the head pairs
-  // of a group share an XCD, consecutive groups rotate over the 8 XCDs
+  // ---- (sequence, query tile, KV head) group and head pair. Workgroup ids
+  // are dealt round-robin to the 8 XCDs; group grow * 8 + xcd runs on XCD
+  // xcd, so its KV head (the group index modulo hkv) is fixed per XCD and
+  // each XCD's L2 holds the K/V of its own heads only (8x less L2-to-fabric
+  // traffic on the 128K launch than rotating groups over the XCDs); the head
+  // pairs of a group share its XCD
   const int pairs = p.g >> 1;
   const int id = blockIdx.x;
   const int xcd = id & 7, rest = id >> 3;
   const int pair = rest % pairs;
   const int grow = rest / pairs;
-  int grp = grow * 8 + ((xcd - grow) & 7);
+  int grp = grow * 8 + xcd;
   if (grp >= p.n_groups) return;
   // visible key tiles of the unit as the launch-order pre-pass counted them
   // (-1: not known, search below)
