@@ -113,6 +113,10 @@ SMALL = [
                                       interleave=8)),
     ("decode_400seqs_split1024", dict(kind="decode", batch=400, len_range=(1, 6000), lengths=(), cp=2, rank=0,
                                       interleave=8, hq=8, hkv=2)),
+    # no context parallelism (cp = 1): the rank holds every token, one step, nothing to merge with
+    ("passkv_cp1_whole", dict(kind="pass_kv", lengths=(700, 130, 1), batch=3, len_range=(), cp=1, rank=0)),
+    ("passq_cp1_whole", dict(kind="pass_q", batch=2, cached=500, new=200, cp=1, rank=0, interleave=8)),
+    ("decode_cp1_whole", dict(kind="decode", batch=8, len_range=(1, 2000), lengths=(), cp=1, rank=0, interleave=8)),
     # one 200K-token context and a short one: 196 splits of 512 local tokens for the long one
     ("decode_long_200k_split512", dict(kind="decode", batch=2, lengths=(200000, 37), len_range=(), cp=2, rank=1,
                                        interleave=8)),
