@@ -467,6 +467,22 @@ def power_probe(seconds: float = 5.0):
     pw = first("/sys/class/drm/card*/device/hwmon/hwmon*/power1_average") or \
         first("/sys/class/drm/card*/device/hwmon/hwmon*/power1_input")
     sclk = first("/sys/class/drm/card*/device/pp_dpm_sclk")
+    temps = {}  # label -> file
+    for f in sorted(glob.glob("/sys/class/drm/card*/device/hwmon/hwmon*/temp*_input")):
+        try:
+            label = open(f.replace("_input", "_label")).read().strip()
+        except OSError:
+            label = os.path.basename(f)
+        temps.setdefault(label, f)
+
+    def read_temps():
+        out = {}
+        for label, f in temps.items():
+            try:
+                out[label] = int(open(f).read()) / 1000.0
+            except (OSError, ValueError):
+                pass
+        return out
 
     def sample():
         w = mhz = None
@@ -483,11 +499,12 @@ def power_probe(seconds: float = 5.0):
         return w, mhz
 
     def run(label, fn, flops=None):
-        samples, done = [], threading.Event()
+        samples, tsamples, done = [], [], threading.Event()
 
         def sampler():
             while not done.is_set():
                 samples.append(sample())
+                tsamples.append(read_temps())
                 time.sleep(0.1)
 
         fn()
@@ -512,6 +529,11 @@ def power_probe(seconds: float = 5.0):
                "power_W_median": ws[len(ws) // 2] if ws else None, "sclk_MHz_median": cs[len(cs) // 2] if cs else None}
         if flops:
             out["TFLOPs"] = round(flops * n / el / 1e12, 1)
+        steady_t = tsamples[len(tsamples) // 5:]
+        for lab in temps:
+            v = sorted(t[lab] for t in steady_t if lab in t)
+            if v:
+                out[f"temp_{lab}_C_median"] = v[len(v) // 2]
         print(json.dumps(out), flush=True)
 
     a = torch.randn(8192, 8192, device="cuda", dtype=torch.bfloat16)
