@@ -643,7 +643,7 @@ def test_full_size_workload(cpa, wl, harness, name):
     torch.cuda.synchronize()
     _row_properties(inp, run)
     cu, pos = inp["cu_q_host"], inp["q_positions_host"]
-    rows = None if name in ALL_ROWS else sample_rows(cu, pos, n_random=48, seed=w.seed)
+    rows = None if name in ALL_ROWS else sample_rows(cu, pos, n_random=192, seed=w.seed)
     if w.kind == "pass_kv":
         rows_, parts, merged = expected_pass_kv(inp, rows)
         # exact -inf pattern on every row of every step, from positions alone
